@@ -1,0 +1,149 @@
+"""The oracle: TEST INFRASTRUCTURE ONLY.
+
+A plain fp64 CPU statement of C = s_a*s_b * A . op(B) (+ bias) over the
+exactly decoded low-precision inputs, plus the format decoders and the
+round-to-nearest-even encoders it needs (all in ``oracle.c``).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP
+library (``tiled_matrix_multiplication_amd``) and never imports it.
+
+Every function here is pinned by ``tests/test_oracle.py`` against facts that
+do not come from the oracle itself (brute force, closed forms, the block
+decomposition identity of the "GEMM to FlashAttention" page's tiling figure,
+and independent library conversions for the codecs).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# The oracle's own format codes (oracle.c numbering).
+F32, BF16, F16, E4M3 = 0, 1, 2, 3
+_NAMES = {"f32": F32, "bf16": BF16, "f16": F16, "e4m3": E4M3}
+_BITS = {F32: np.uint32, BF16: np.uint16, F16: np.uint16, E4M3: np.uint8}
+
+
+def build(verbose: bool = False) -> str:
+    """Compile oracle.c with gcc into liboracle.so (plain C, -O2, OpenMP)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
+    lib.oracle_decode.argtypes = [ctypes.c_int, vp, vp, i64]
+    lib.oracle_round.argtypes = [ctypes.c_int, vp, vp, i64]
+    lib.oracle_gemm.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, vp, i64,
+                                ctypes.c_int, vp, dp, dp, vp, i64, vp]
+    lib.oracle_threads.argtypes = []
+    for f in (lib.oracle_decode, lib.oracle_round, lib.oracle_gemm, lib.oracle_threads):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _fmt(fmt) -> int:
+    return _NAMES[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def decode(fmt, bits: np.ndarray) -> np.ndarray:
+    """Exact float64 values of an array of format bit patterns."""
+    f = _fmt(fmt)
+    bits = np.ascontiguousarray(bits, dtype=_BITS[f])
+    out = np.empty(bits.shape, dtype=np.float64)
+    rc = _load().oracle_decode(f, _ptr(bits), _ptr(out), bits.size)
+    if rc:
+        raise ValueError(f"oracle_decode failed ({rc})")
+    return out
+
+
+def round_to(fmt, x: np.ndarray) -> np.ndarray:
+    """Bit patterns of the bf16/fp16 values nearest to x (ties to even)."""
+    f = _fmt(fmt)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    rc = _load().oracle_round(f, _ptr(x), _ptr(out), x.size)
+    if rc:
+        raise ValueError(f"oracle_round failed ({rc})")
+    return out
+
+
+def gemm(fmt, A: np.ndarray, B: np.ndarray, trans_b: bool = False,
+         bias: np.ndarray | None = None, scale_a: float = 1.0,
+         scale_b: float = 1.0, want_abs: bool = False):
+    """o = s_a*s_b * A . op(B) (+ bias) in float64.
+
+    A: (M, K) bit patterns of ``fmt``; B: (K, N) bit patterns, or (N, K) when
+    ``trans_b``.  Row strides of the given arrays are honoured as leading
+    dimensions.  Returns o (M, N) float64, and with ``want_abs`` also
+    T = sum_k |a_ik b'_kj| (same shape).
+    """
+    f = _fmt(fmt)
+    A = np.asarray(A)
+    B = np.asarray(B)
+    if A.dtype != _BITS[f] or B.dtype != _BITS[f]:
+        raise TypeError("A and B must hold the format's bit patterns")
+    if A.ndim != 2 or B.ndim != 2:
+        raise ValueError("A and B must be 2-D")
+    A = _rowmajor(A)
+    B = _rowmajor(B)
+    M, K = A.shape
+    if trans_b:
+        N, K2 = B.shape
+    else:
+        K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    lda = A.strides[0] // A.itemsize if M > 1 else max(K, 1)
+    ldb = B.strides[0] // B.itemsize if B.shape[0] > 1 else max(B.shape[1], 1)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.shape != (N,):
+            raise ValueError("bias must have N entries")
+    C = np.empty((M, N), dtype=np.float64)
+    T = np.empty((M, N), dtype=np.float64) if want_abs else None
+    rc = _load().oracle_gemm(M, N, K, f, _ptr(A), lda, _ptr(B), ldb, int(bool(trans_b)),
+                             _ptr(bias), float(scale_a), float(scale_b), _ptr(C),
+                             max(N, 1), _ptr(T))
+    if rc:
+        raise ValueError(f"oracle_gemm failed ({rc})")
+    return (C, T) if want_abs else C
+
+
+def threads() -> int:
+    """Threads the oracle's product runs on (OpenMP, from OMP_NUM_THREADS)."""
+    return int(_load().oracle_threads())
+
+
+def _rowmajor(X: np.ndarray) -> np.ndarray:
+    """A view whose elements along a row are adjacent (copy otherwise)."""
+    if X.shape[1] <= 1 or X.strides[1] == X.itemsize:
+        if X.strides[0] >= 0 and X.strides[0] % X.itemsize == 0:
+            return X
+    return np.ascontiguousarray(X)

@@ -1,0 +1,278 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU statement of what the GPU library
+ * computes.  Only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this file's library.  It shares no code, header, table
+ * or helper with the HIP library; it never calls it and is never called by it.
+ *
+ * What it computes (all in IEEE double precision):
+ *
+ *   o[i][j] = s_a * s_b * sum_{k<K} a[i][k] * b'[k][j]  (+ bias[j])
+ *
+ *   - the definition C[i][j] = sum_k A[i][k]*B[k][j] with a float64
+ *     accumulator: "GEMM to FlashAttention" page (youngju.dev), the
+ *     naive_matmul listing;
+ *   - op(B) = B or B^T selected by a transpose flag, leading dimensions as
+ *     memory strides: same page, the BLAS "GEMM interface" box;
+ *   - the bias is one value per output feature, added after the product:
+ *     same page, the linear-layer formula at its top, and CMU 15-418
+ *     Lecture 27 notes (runguoli.com) section 2.1 (fully connected layer =
+ *     matrix-vector product plus b);
+ *   - inputs are stored in a low-precision format and the products are summed
+ *     at higher precision: Lecture 27 notes section 2.7 (formats figure and
+ *     Table 1).  Here the sum is exact-ish fp64 over the exactly decoded
+ *     inputs, which is the plain definition the fp32-accumulating kernels
+ *     approximate.
+ *
+ * Input formats are decoded exactly from their bit patterns by the decoders
+ * below, each written from the format's definition (Lecture 27 notes
+ * section 2.7 gives the bit splits: fp32 1+8+23, bf16 1+8+7, fp8 E4M3 1+4+3
+ * with range to 448; fp16 is IEEE binary16, 1+5+10).
+ *
+ * Output rounding R(o) to bf16 / fp16 is "round to the nearest representable
+ * value, ties to the even significand", written from that definition on the
+ * format's grid of representable values.
+ *
+ * Each pin of this file lives in tests/test_oracle.py.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* The oracle's own format codes (its own numbering). */
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_F16 2
+#define ORC_E4M3 3
+
+/* ---------------- decoders: bit pattern -> exact double ---------------- */
+
+static double dec_f32(uint32_t u) {
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* bf16 is the upper half of an fp32 pattern: same sign and exponent field,
+ * the top 7 of the 23 fraction bits. */
+static double dec_bf16(uint16_t u) { return dec_f32((uint32_t)u << 16); }
+
+/* IEEE binary16: sign, 5-bit exponent (bias 15), 10-bit fraction. */
+static double dec_f16(uint16_t u) {
+  int s = (u >> 15) & 1;
+  int e = (u >> 10) & 0x1f;
+  int m = u & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-14 * 2^-10 */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp(1024.0 + m, e - 25); /* (1 + m/2^10) * 2^(e-15) */
+  return s ? -v : v;
+}
+
+/* OCP fp8 E4M3 ("fn"): sign, 4-bit exponent (bias 7), 3-bit fraction, no
+ * infinities, S.1111.111 is NaN, largest finite 1.75 * 2^8 = 448. */
+static double dec_e4m3(uint8_t u) {
+  int s = (u >> 7) & 1;
+  int e = (u >> 3) & 0xf;
+  int m = u & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9); /* m/8 * 2^-6 */
+  else
+    v = ldexp(8.0 + m, e - 10); /* (1 + m/8) * 2^(e-7) */
+  return s ? -v : v;
+}
+
+static double dec_at(int fmt, const void *p, int64_t idx) {
+  switch (fmt) {
+  case ORC_F32:
+    return dec_f32(((const uint32_t *)p)[idx]);
+  case ORC_BF16:
+    return dec_bf16(((const uint16_t *)p)[idx]);
+  case ORC_F16:
+    return dec_f16(((const uint16_t *)p)[idx]);
+  case ORC_E4M3:
+    return dec_e4m3(((const uint8_t *)p)[idx]);
+  default:
+    return NAN;
+  }
+}
+
+int oracle_decode(int fmt, const void *src, double *dst, int64_t n) {
+  if (fmt < ORC_F32 || fmt > ORC_E4M3 || n < 0)
+    return -1;
+  for (int64_t i = 0; i < n; ++i)
+    dst[i] = dec_at(fmt, src, i);
+  return 0;
+}
+
+/* ---------------- rounding: double -> nearest format value ---------------- */
+
+/*
+ * Round x to the grid of a binary format with `p` significant bits and
+ * smallest normal exponent `emin` (values are (1.f) * 2^e, e >= emin, and
+ * subnormals share the grid spacing 2^(emin-p+1)).  Ties go to the value
+ * whose last significand bit is zero: rint() in the default rounding mode
+ * does exactly that on the integer grid x / quantum.
+ */
+static double round_to_grid(double x, int p, int emin) {
+  if (x == 0.0 || !isfinite(x))
+    return x;
+  int ex;
+  frexp(fabs(x), &ex); /* |x| = f * 2^ex, f in [0.5, 1): exponent e = ex-1 */
+  int e = ex - 1;
+  if (e < emin)
+    e = emin;
+  double quantum = ldexp(1.0, e - (p - 1));
+  return rint(x / quantum) * quantum; /* x/quantum and the product are exact */
+}
+
+/* bf16: 8 significant bits, emin = -126, largest finite (2 - 2^-7) * 2^127. */
+static uint16_t enc_bf16(double x) {
+  if (isnan(x))
+    return 0x7fc0;
+  double r = round_to_grid(x, 8, -126);
+  /* r is exactly representable in bf16 unless it overflowed past the top
+   * binade, in which case it rounded up to 2^128: infinity. */
+  if (fabs(r) >= ldexp(1.0, 128))
+    return signbit(x) ? 0xff80 : 0x7f80;
+  float f = (float)r; /* exact: r has at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+/* fp16: 11 significant bits, emin = -14, largest finite 65504. */
+static uint16_t enc_f16(double x) {
+  if (isnan(x))
+    return 0x7e00;
+  double r = round_to_grid(x, 11, -14);
+  uint16_t s = signbit(x) ? 0x8000 : 0;
+  double a = fabs(r);
+  if (a >= 65536.0)
+    return s | 0x7c00;
+  if (a == 0.0)
+    return s;
+  if (a < ldexp(1.0, -14)) /* subnormal: a = m * 2^-24 */
+    return s | (uint16_t)(a * ldexp(1.0, 24));
+  int ex;
+  double f = frexp(a, &ex);         /* a = f * 2^ex, f in [0.5,1) */
+  int e = ex - 1;                   /* a = (2f) * 2^e, 2f in [1,2) */
+  double frac = (2.0 * f - 1.0) * 1024.0; /* exact integer 0..1023 */
+  return s | (uint16_t)((e + 15) << 10) | (uint16_t)frac;
+}
+
+int oracle_round(int fmt, const double *src, uint16_t *dst, int64_t n) {
+  if (n < 0)
+    return -1;
+  if (fmt == ORC_BF16) {
+    for (int64_t i = 0; i < n; ++i)
+      dst[i] = enc_bf16(src[i]);
+    return 0;
+  }
+  if (fmt == ORC_F16) {
+    for (int64_t i = 0; i < n; ++i)
+      dst[i] = enc_f16(src[i]);
+    return 0;
+  }
+  return -1;
+}
+
+/* ---------------- the product ---------------- */
+
+/*
+ * o = s_a*s_b * A . op(B) (+ bias), everything decoded to double first.
+ *
+ *   A  : M rows of K elements, row i starts at element i*lda
+ *   B  : trans_b == 0 -> K rows of N elements (row k at k*ldb), b'[k][j] = B[k][j]
+ *        trans_b != 0 -> N rows of K elements (row j at j*ldb), b'[k][j] = B[j][k]
+ *   bias: NULL or N float32 values, added to every row
+ *   C  : M rows of N doubles at stride ldc (written, not accumulated into)
+ *   T  : NULL or M rows of N doubles at stride ldc, T[i][j] = sum_k |a_ik b'_kj|
+ *        (the scale of the rounding error bound of any summation order)
+ *
+ * Loop order i, k, j with a double row accumulator.  Rows are independent,
+ * so they are spread over OpenMP threads; each row's sum is formed the same
+ * way whatever the thread count.
+ */
+int oracle_gemm(int64_t M, int64_t N, int64_t K, int fmt, const void *A,
+                int64_t lda, const void *B, int64_t ldb, int trans_b,
+                const float *bias, double scale_a, double scale_b, double *C,
+                int64_t ldc, double *T) {
+  if (M < 0 || N < 0 || K < 0 || fmt < ORC_F32 || fmt > ORC_E4M3)
+    return -1;
+  if (lda < K || ldc < N || ldb < (trans_b ? K : N))
+    return -2;
+  if (M == 0 || N == 0)
+    return 0;
+
+  /* b' as a K x N double matrix (row k contiguous). */
+  double *bp = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1) * (size_t)N);
+  if (!bp)
+    return -3;
+  for (int64_t k = 0; k < K; ++k)
+    for (int64_t j = 0; j < N; ++j)
+      bp[k * N + j] = trans_b ? dec_at(fmt, B, j * ldb + k) : dec_at(fmt, B, k * ldb + j);
+
+  const double scale = scale_a * scale_b; /* exact: two floats' product fits a double */
+  int fail = 0;
+
+#pragma omp parallel
+  {
+    double *acc = (double *)malloc(sizeof(double) * (size_t)N);
+    double *tab = T ? (double *)malloc(sizeof(double) * (size_t)N) : NULL;
+    if (!acc || (T && !tab)) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+          acc[j] = 0.0;
+          if (tab)
+            tab[j] = 0.0;
+        }
+        for (int64_t k = 0; k < K; ++k) {
+          const double a = dec_at(fmt, A, i * lda + k);
+          const double *brow = bp + k * N;
+          for (int64_t j = 0; j < N; ++j)
+            acc[j] += a * brow[j];
+          if (tab)
+            for (int64_t j = 0; j < N; ++j)
+              tab[j] += fabs(a * brow[j]);
+        }
+        for (int64_t j = 0; j < N; ++j) {
+          double v = scale * acc[j];
+          if (bias)
+            v += (double)bias[j];
+          C[i * ldc + j] = v;
+          if (tab)
+            T[i * ldc + j] = fabs(scale) * tab[j];
+        }
+      }
+    }
+    free(acc);
+    free(tab);
+  }
+  free(bp);
+  return fail ? -3 : 0;
+}
+
+/* Number of threads the product above runs on. */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
