@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Throughput of the tiled GEMM / GEMV library on one MI355X.
+
+Default run: the headline workload, a bf16 GEMM C = A . B with
+M = N = K = 4096 (NN, fp32 output, no bias), timed over --steps launches
+after --warmup untimed ones, with the inputs resident in HBM and rotated over
+several copies so consecutive launches do not hit in the 256 MiB MALL.  One
+JSON line is printed with:
+  value      TFLOP/s = 2 M N K / t  (the metric of the "GEMM to FlashAttention"
+             page's benchmark listing and roofline section),
+  roofline   achieved vs the dense bf16 MFMA peak (2516.6 TFLOP/s),
+  gemv       the M = 1 decode GEMV (W 4096 x 4096 bf16, + bias, bf16 y) in
+             GB/s of algorithmic bytes vs 8 TB/s HBM, rotated over 20 copies
+             of W (640 MiB > MALL),
+  cpu_baseline  the fp64 oracle on the host cores over a bounded row sample
+             of the same product (the sample's GPU rows are also compared).
+
+--workload picks another workload (linear layers, attention products, fp8,
+ragged shapes, fp32) and prints its line in the same form; --gpus > 1 is not
+supported (one GPU per process, nothing is sharded here).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s (2MNK/t) bf16 4096³ and % of MFMA peak; GEMV GB/s % HBM peak"
+
+# MI355X published peaks (dense, no sparsity).
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+BYTES = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1}
+
+
+# ---------------------------------------------------------------- algorithmic work
+
+
+def gemm_flops(M, N, K, batch=1):
+    """2 M N K per problem: one multiply and one add per term of every sum."""
+    return 2.0 * M * N * K * batch
+
+
+def gemm_bytes(M, N, K, in_bytes, out_bytes, batch=1, bias=False):
+    """Compulsory traffic: read A and B once, write C once (+ the fp32 bias)."""
+    return float(batch * ((M * K + K * N) * in_bytes + M * N * out_bytes) + (4 * N if bias else 0))
+
+
+def intensity(M, N, K, in_bytes, out_bytes=None):
+    """FLOP per compulsory byte (the arithmetic intensity of the roofline model)."""
+    out_bytes = in_bytes if out_bytes is None else out_bytes
+    return gemm_flops(M, N, K) / gemm_bytes(M, N, K, in_bytes, out_bytes)
+
+
+def roofline_time(flops, nbytes, peak_tflops, peak_gbs=PEAK_HBM_GBS):
+    """Lower bound on time: min(peak, bandwidth x intensity) turned into seconds."""
+    return max(flops / (peak_tflops * 1e12), nbytes / (peak_gbs * 1e9))
+
+
+# ---------------------------------------------------------------- workloads
+
+WORKLOADS = {
+    # name: (M, N, K, batch, in, out, trans_b, bias)
+    "square_bf16": (4096, 4096, 4096, 1, "bf16", "f32", False, False),
+    "qkv": (8192, 12288, 4096, 1, "bf16", "bf16", True, True),
+    "ffn_up": (8192, 14336, 4096, 1, "bf16", "bf16", True, True),
+    "ffn_down": (8192, 4096, 14336, 1, "bf16", "bf16", True, True),
+    "attn_scores": (2048, 2048, 128, 128, "f16", "f16", True, False),
+    "attn_output": (2048, 128, 2048, 128, "f16", "f16", False, False),
+    "fp8_square": (8192, 8192, 8192, 1, "e4m3", "bf16", False, False),
+    "ragged_1000x3000x777": (1000, 3000, 777, 1, "bf16", "bf16", False, False),
+    "ragged_4097x511x1023": (4097, 511, 1023, 1, "bf16", "bf16", False, False),
+    "f32_256": (256, 256, 256, 1, "f32", "f32", False, False),
+    "gemv": (1, 4096, 4096, 1, "bf16", "bf16", True, True),
+}
+
+
+def describe(name):
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    lay = "NT" if tb else "NN"
+    b = f"batch {Z} x " if Z > 1 else ""
+    if name == "gemv":
+        return f"{fin} GEMV y = W.x + bias, W {N}x{K}, {fout} y"
+    return f"{fin} GEMM {b}{M}x{N}x{K} {lay}, {fout} out{', fp32 bias' if bias else ''}"
+
+
+def make_inputs(name, copies, dev):
+    """Seeded synthetic operands of a workload, `copies` distinct device copies."""
+    import torch
+
+    import synthetic as syn
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    cfg = {"square_bf16": 2, "qkv": 3, "ffn_up": 3, "ffn_down": 3, "gemv": 3, "attn_scores": 4,
+           "attn_output": 4, "fp8_square": 5}.get(name, 5)
+    ashape = (Z, M, K) if Z > 1 else (M, K)
+    bshape = ((Z, N, K) if tb else (Z, K, N)) if Z > 1 else ((N, K) if tb else (K, N))
+    sa = sb = 1.0
+    if name == "attn_output":
+        A = syn.softmax_rows_f16(Z, M, syn.seed_of(4, "logits"))
+        B = syn.to_bits(syn.normal(bshape, syn.seed_of(4, "V")), fin)
+    elif fin == "e4m3":
+        xa = syn.normal(ashape, syn.seed_of(cfg, "A"))
+        xb = syn.normal(bshape, syn.seed_of(cfg, "B"))
+        sa, sb = syn.e4m3_scale(xa), syn.e4m3_scale(xb)
+        A, B = syn.quantize_e4m3(xa, sa), syn.quantize_e4m3(xb, sb)
+    else:
+        wstd = 0.02 if tb and Z == 1 else 1.0   # linear-layer weights ~ N(0, 0.02^2)
+        xa = syn.normal(ashape, syn.seed_of(cfg, "A"))
+        xb = syn.normal(bshape, syn.seed_of(cfg, "B"), std=wstd)
+        A, B = syn.to_bits(xa, fin), syn.to_bits(xb, fin)
+    bvec = syn.normal((N,), syn.seed_of(cfg, "bias"), 0.02) if bias else None
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[fout]
+    sets = []
+    hA, hB = syn.as_torch(A, fin), syn.as_torch(B, fin)
+    for _ in range(copies):
+        dA, dB = hA.to(dev), hB.to(dev)
+        dC = torch.empty((Z, M, N) if Z > 1 else (M, N), dtype=tdt, device=dev)
+        sets.append((dA, dB, dC))
+    dbias = torch.from_numpy(bvec).to(dev) if bvec is not None else None
+    return sets, dbias, (A, B, bvec, float(sa), float(sb))
+
+
+def launcher(name, sets, dbias, sa, sb):
+    import tiled_matrix_multiplication_amd as tmm
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    if name == "gemv":
+        def run(i):
+            W, x, y = sets[i % len(sets)]
+            tmm.tmm_gemv(W, x.view(-1)[:K], y.view(-1), bias=dbias)
+    elif Z > 1:
+        def run(i):
+            A, B, C = sets[i % len(sets)]
+            tmm.tmm_gemm_strided_batched(A, B, C, bias=dbias, trans_b=tb)
+    else:
+        def run(i):
+            A, B, C = sets[i % len(sets)]
+            tmm.tmm_gemm(A, B, C, bias=dbias, trans_b=tb, scale_a=sa, scale_b=sb)
+    return run
+
+
+def time_steps(run, steps, warmup):
+    """Average ms per launch from HIP events on the launching (current) stream."""
+    import torch
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        run(warmup + i)
+    end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def copies_for(name):
+    """Enough distinct input copies that a launch finds its operands out of the MALL."""
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    per = Z * ((M * K + K * N) * BYTES[fin] + M * N * BYTES[fout])
+    return int(max(1, min(20, np.ceil(600e6 / per))))
+
+
+def measure(name, steps, warmup, dev):
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    copies = copies_for(name)
+    if name == "gemv":
+        import torch
+
+        import synthetic as syn
+        W = syn.to_bits(syn.normal((N, K), syn.seed_of(3, "B"), 0.02), fin)
+        x = syn.to_bits(syn.normal((1, K), syn.seed_of(3, "A")), fin)
+        hW, hx = syn.as_torch(W, fin), syn.as_torch(x, fin)
+        sets = [(hW.to(dev), hx.to(dev), torch.empty((N,), dtype=torch.bfloat16, device=dev))
+                for _ in range(copies)]
+        dbias = torch.from_numpy(syn.normal((N,), syn.seed_of(3, "bias"), 0.02)).to(dev)
+        host = (x, W, None, 1.0, 1.0)
+        sa = sb = 1.0
+    else:
+        sets, dbias, host = make_inputs(name, copies, dev)
+        sa, sb = host[3], host[4]
+    run = launcher(name, sets, dbias, sa, sb)
+    ms, wall = time_steps(run, steps, warmup)
+    flops = gemm_flops(M, N, K, Z)
+    nbytes = gemm_bytes(M, N, K, BYTES[fin], BYTES[fout], Z, bias)
+    return {"ms": ms, "wall": wall, "flops": flops, "bytes": nbytes, "copies": copies,
+            "sets": sets, "host": host}
+
+
+def roofline_entry(name, r):
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    t = r["ms"] * 1e-3
+    ai = r["flops"] / r["bytes"]
+    ridge = PEAK_TFLOPS[fin] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai >= ridge:
+        ach = r["flops"] / t / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_TFLOPS[fin], "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_TFLOPS[fin], 4), "traffic": None}
+    ach = r["bytes"] / t / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+
+def compare_rows(C, idx, o):
+    """Relative Frobenius difference of GPU output rows `idx` from oracle rows `o`."""
+    import torch
+    g = C[torch.as_tensor(idx, device=C.device)].float().cpu().numpy().astype(np.float64)
+    den = float(np.linalg.norm(o))
+    return float(np.linalg.norm(g - o) / den) if den > 0 else float(np.linalg.norm(g - o))
+
+
+def cpu_baseline(name, r, target_s=12.0):
+    """The oracle, as it stands, on a row sample of the workload's first problem.
+
+    Times it on the host cores (OpenMP threads), scales to the metric's unit,
+    and compares the sampled GPU rows against it."""
+    import oracle
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    A, B, bvec, sa, sb = r["host"]
+    if Z > 1:
+        A, B = A[0], B[0]
+    rng = np.random.default_rng(12345)
+
+    def run_rows(rows):
+        idx = np.sort(rng.choice(M, size=rows, replace=False)) if rows < M else np.arange(M)
+        t0 = time.perf_counter()
+        o = oracle.gemm(fin, np.ascontiguousarray(A[idx]), B, trans_b=tb, bias=bvec, scale_a=sa, scale_b=sb)
+        return idx, o, time.perf_counter() - t0
+
+    rows = min(M, 8)
+    idx, o, t = run_rows(rows)
+    if t < target_s / 4 and rows < M:
+        rows = int(min(M, max(rows, rows * target_s / max(t, 1e-3))))
+        idx, o, t = run_rows(rows)
+    flops = gemm_flops(len(idx), N, K)
+    C = r["sets"][0][2]
+    C0 = C[0] if Z > 1 else C
+    err = compare_rows(C0, idx, o)
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": round(t, 2),
+            "sample": f"{len(idx)} of {M} rows of the {describe(name)} product "
+                      f"({len(idx)}x{N}x{K}, fp64 triple loop)",
+            "sample_rel_fro_vs_gpu": err}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="square_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-gemv", action="store_true", help="skip the GEMV side measurement")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this library runs on one GPU per "
+              "process and shards nothing (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    import tiled_matrix_multiplication_amd  # noqa: F401  (fails loudly without libtmm.so)
+    dev = "cuda:0"
+    name = args.workload
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+
+    r = measure(name, args.steps, args.warmup, dev)
+    roof = roofline_entry(name, r)
+    value = r["flops"] / (r["ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC if name == "square_bf16" else f"{describe(name)}: TFLOP/s (2MNK/t)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": fin,
+        "data": "synthetic",
+        "config": {"workload": describe(name), "M": M, "N": N, "K": K, "batch": Z,
+                   "layout": "NT" if tb else "NN", "out": fout, "bias": bias,
+                   "input_copies_rotated": r["copies"]},
+        "roofline": roof,
+    }
+    if name == "square_bf16" and not args.no_gemv:
+        g = measure("gemv", max(200, args.steps), max(20, args.warmup), dev)
+        gbs = g["bytes"] / (g["ms"] * 1e-3) / 1e9
+        line["gemv"] = {"workload": describe("gemv"), "us_per_launch": round(g["ms"] * 1e3, 3),
+                        "bytes_per_launch": int(g["bytes"]), "achieved": round(gbs, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "weight_copies_rotated": g["copies"]}
+        del g
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(name, r)
+    line["wall_s_timed"] = round(r["wall"], 4)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

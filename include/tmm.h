@@ -1,0 +1,142 @@
+/*
+ * tmm.h -- tiled dense matrix multiplication on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libtmm.so.  Three entry points compute
+ *
+ *     C = scale_a * scale_b * A . op(B)  (+ bias broadcast over rows)
+ *
+ * for one matrix (tmm_gemm), for a batch of equally shaped matrices at fixed
+ * element strides (tmm_gemm_strided_batched), and for the matrix-vector case
+ * y = W . x (+ bias) (tmm_gemv).
+ *
+ * Sources of the operation:
+ *   - product definition C[i][j] = sum_k A[i][k] * B[k][j], A (M,K), B (K,N):
+ *     "GEMM to FlashAttention" page (youngju.dev), naive_matmul listing;
+ *   - the BLAS interface C = alpha*op(A)*op(B) + beta*C with transpose flags,
+ *     dimensions m, n, k and leading dimensions lda/ldb/ldc as memory strides:
+ *     same page, "GEMM interface" box.  Here only op(B) may be transposed,
+ *     alpha is the product of two fp8 dequantisation scales, and beta is 0
+ *     (C is overwritten, never read);
+ *   - bias as one value per output feature added after the product, weights
+ *     stored (out_features, in_features): same page, linear-layer formula;
+ *     CMU 15-418 Lecture 27 notes (runguoli.com) section 2.1, fully
+ *     connected layer as a matrix-vector product plus b;
+ *   - low-precision inputs with fp32 accumulation: Lecture 27 notes section
+ *     2.7 (formats, Table 1, "accumulate in higher precision");
+ *   - matrix-vector product as the memory-bound Level-2 case: "GEMM to
+ *     FlashAttention" page, BLAS levels list; Lecture 27 notes section 7,
+ *     question 1 (batch-1 y = W x).
+ *
+ * Layout: every matrix is row-major.  Element (r, c) of a matrix with
+ * leading dimension ld is at element offset r*ld + c from its pointer.
+ *   A : M x K, lda >= max(1, K)
+ *   B : trans_b == 0 -> K x N, ldb >= max(1, N)       (op(B) = B,   "NN")
+ *       trans_b != 0 -> N x K, ldb >= max(1, K)       (op(B) = B^T, "NT";
+ *                                                      a linear layer's W)
+ *   C : M x N, ldc >= max(1, N)
+ *   bias : NULL, or N float32 values (bias[j] is added to column j)
+ *
+ * Types (ab_type -> allowed c_type):
+ *   TMM_F32    -> TMM_F32
+ *   TMM_BF16   -> TMM_F32, TMM_BF16
+ *   TMM_F16    -> TMM_F32, TMM_F16
+ *   TMM_F8E4M3 -> TMM_F32, TMM_BF16        (OCP E4M3, largest finite 448)
+ * Products are summed in fp32; a rounded output (bf16/fp16) is rounded once,
+ * to nearest even, after scale and bias.  fp16 subnormal inputs and outputs
+ * are kept, never flushed.  scale_a and scale_b must be 1 unless ab_type is
+ * TMM_F8E4M3; they are the per-tensor dequantisation factors of A and B.
+ *
+ * Ownership: every pointer is device memory owned by the caller.  The library
+ * allocates nothing, keeps no pointer after returning, holds no state between
+ * calls and may be called from several host threads at once.  Work is
+ * enqueued on `stream` (NULL = the default stream) and the call returns
+ * without waiting for it.  C must not overlap A, B or bias.
+ *
+ * Errors: each call returns TMM_OK (0) or one of the negative codes below.
+ * Argument checks run on the host before any HIP call; a failing call
+ * enqueues nothing, prints nothing and never exits.  TMM_ERR_LAUNCH reports a
+ * HIP error seen right after the launch.
+ *
+ * Quick returns: M == 0, N == 0 or batch == 0 enqueue nothing and return 0
+ * (pointers are not checked then).  K == 0 is the empty sum: C = bias (or 0).
+ */
+#ifndef TMM_H
+#define TMM_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tmm_dtype {
+  TMM_F32 = 0,
+  TMM_BF16 = 1,
+  TMM_F16 = 2,
+  TMM_F8E4M3 = 3
+} tmm_dtype;
+
+enum tmm_status {
+  TMM_OK = 0,
+  TMM_ERR_DIM = -1,    /* M, N, K or batch negative                          */
+  TMM_ERR_LD = -2,     /* a leading dimension below its row length (or < 1)  */
+  TMM_ERR_NULL = -3,   /* NULL pointer for an operand with non-zero extent    */
+  TMM_ERR_DTYPE = -4,  /* unknown type or a type pair not in the table above  */
+  TMM_ERR_SCALE = -5,  /* scale != 1 for a non-fp8 type, or a non-finite one  */
+  TMM_ERR_STRIDE = -6, /* negative batch stride, or C matrices that overlap   */
+  TMM_ERR_ALIGN = -7,  /* pointer not aligned to its element size            */
+  TMM_ERR_LAUNCH = -8  /* HIP reported an error at launch                     */
+};
+
+/*
+ * C = scale_a*scale_b * A . op(B) (+ bias).  M x N outputs, K-long sums.
+ * A, B, C, bias and the dimensions as described above.
+ */
+int tmm_gemm(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type,
+             tmm_dtype c_type, int trans_b, const void *A, int64_t lda,
+             const void *B, int64_t ldb, void *C, int64_t ldc,
+             const float *bias, float scale_a, float scale_b,
+             hipStream_t stream);
+
+/*
+ * The same product for batch = 0, 1, 2, ... independent problems:
+ *   C + z*strideC = scale_a*scale_b * (A + z*strideA) . op(B + z*strideB) (+ bias)
+ * Strides are in elements and must be >= 0 (0 repeats one operand for every
+ * problem).  For batch > 1 the C matrices must not overlap:
+ * strideC >= (M-1)*ldc + N.  The one bias vector serves every problem.
+ * This is the form of attention's two products, scores = Q . K^T (NT) and
+ * output = weights . V (NN), over batch x heads: "GEMM to FlashAttention"
+ * page, attention_standard listing.
+ */
+int tmm_gemm_strided_batched(int64_t M, int64_t N, int64_t K,
+                             tmm_dtype ab_type, tmm_dtype c_type, int trans_b,
+                             const void *A, int64_t lda, int64_t strideA,
+                             const void *B, int64_t ldb, int64_t strideB,
+                             void *C, int64_t ldc, int64_t strideC,
+                             int64_t batch, const float *bias, float scale_a,
+                             float scale_b, hipStream_t stream);
+
+/*
+ * y[n] = sum_k W[n][k] * x[k] (+ bias[n]),  n < N, k < K.
+ *   W : N x K row-major (out_features x in_features), ldw >= max(1, K)
+ *   x : K elements of w_type;  y : N elements of y_type
+ * w_type -> y_type as for tmm_gemm, except that TMM_F8E4M3 is not accepted.
+ * A memory-bound stream over W: every weight is read once.
+ */
+int tmm_gemv(int64_t N, int64_t K, tmm_dtype w_type, tmm_dtype y_type,
+             const void *W, int64_t ldw, const void *x, void *y,
+             const float *bias, hipStream_t stream);
+
+/* Static English text of a status code (never NULL). */
+const char *tmm_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int tmm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TMM_H */

@@ -1,0 +1,117 @@
+"""Comparison rules between the HIP path and the oracle.
+
+Tolerances (the pages give none; these follow from the arithmetic):
+  * small-integer inputs: every product and partial sum is an integer below
+    2^24, exact in fp32, so the GPU result must equal the oracle bit for bit,
+    also after rounding to bf16/fp16 (nearest-even on both sides);
+  * fp32 outputs: relative Frobenius error  ||g - o||_F / ||o||_F <= 1e-5;
+  * bf16/fp16 outputs: |g - R(o)| <= 1 ulp(R(o)) elementwise, where R is the
+    oracle's nearest-even rounding; an element that misses this is accepted
+    only where cancellation makes fp32 summation error exceed half an ulp:
+    |g - o| <= ulp(R(o)) + 4 sqrt(K) 2^-24 T  with T = sum_k |a_ik b_kj|
+    (probabilistic fp32 summation bound with lambda = 4);
+  * fp8 inputs: relative Frobenius error <= 1e-3 (fp32 output: against o;
+    bf16 output: against R(o), on top of the 1-ulp rule).  The gfx950 fp8
+    matrix instruction aligns the products of one instruction to the largest
+    one and drops low-order bits (448 + 63 * 2^-9 sums to 448.109375, not
+    448.123046875), so fp8 sums are not held to the fp32 1e-5 figure.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+
+FRO_TOL_F32 = 1e-5
+FRO_TOL_F8 = 1e-3
+LAMBDA = 4.0
+
+_P = {"bf16": (8, -126), "f16": (11, -14)}   # significant bits, smallest normal exponent
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    """Bit patterns of a CPU/GPU tensor as a numpy unsigned array."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    raise TypeError(t.dtype)
+
+
+def fmt_of(t: torch.Tensor) -> str:
+    return {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16",
+            torch.float8_e4m3fn: "e4m3"}[t.dtype]
+
+
+def ulp(fmt: str, v: np.ndarray) -> np.ndarray:
+    p, emin = _P[fmt]
+    a = np.abs(v)
+    e = np.where(a > 0, np.floor(np.log2(np.where(a > 0, a, 1.0))), emin)
+    e = np.maximum(e, emin)
+    return np.ldexp(1.0, (e - (p - 1)).astype(np.int64))
+
+
+def rel_fro(g: np.ndarray, o: np.ndarray) -> float:
+    den = float(np.linalg.norm(o))
+    num = float(np.linalg.norm(g - o))
+    return num / den if den > 0 else num
+
+
+def check_exact(g: torch.Tensor, o: np.ndarray, what: str = ""):
+    """Bit-exact: fp32 output equals o; a rounded output equals R(o)."""
+    f = fmt_of(g)
+    gb = to_bits(g)
+    if f == "f32":
+        gv = oracle.decode("f32", gb)
+        bad = gv != o
+    else:
+        bad = gb != oracle.round_to(f, o)
+    n = int(bad.sum())
+    assert n == 0, f"{what}: {n} of {bad.size} elements differ from the exact result; first at " \
+                   f"{np.argwhere(bad)[0].tolist()}"
+
+
+def check_f32(g: torch.Tensor, o: np.ndarray, tol: float = FRO_TOL_F32, what: str = ""):
+    gv = oracle.decode("f32", to_bits(g))
+    assert np.all(np.isfinite(gv)), f"{what}: non-finite output"
+    err = rel_fro(gv, o)
+    assert err <= tol, f"{what}: relative Frobenius error {err:.3e} > {tol:.0e}"
+    return err
+
+
+def check_rounded(g: torch.Tensor, o: np.ndarray, T: np.ndarray, K: int, what: str = "",
+                  fro_tol: float | None = None):
+    """1-ulp rule for bf16/fp16 outputs, with the cancellation allowance."""
+    f = fmt_of(g)
+    gb = to_bits(g)
+    gv = oracle.decode(f, gb)
+    r = oracle.decode(f, oracle.round_to(f, o))
+    u = ulp(f, r)
+    ok = np.abs(gv - r) <= u
+    bound = LAMBDA * math.sqrt(max(K, 1)) * 2.0 ** -24 * T
+    loose = ~ok & (np.abs(gv - o) <= u + bound)
+    bad = ~(ok | loose)
+    n = int(bad.sum())
+    if n:
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {n} of {bad.size} elements beyond 1 ulp; first {list(i)}: "
+                             f"gpu {gv[i]!r} oracle {o[i]!r} rounded {r[i]!r} ulp {u[i]!r}")
+    if fro_tol is not None:
+        err = rel_fro(gv, r)
+        assert err <= fro_tol, f"{what}: relative Frobenius error {err:.3e} > {fro_tol:.0e}"
+    return int(loose.sum())
+
+
+def check(g: torch.Tensor, o: np.ndarray, T: np.ndarray | None, K: int, exact: bool = False,
+          what: str = "", f8: bool = False):
+    if exact:
+        return check_exact(g, o, what)
+    if fmt_of(g) == "f32":
+        return check_f32(g, o, tol=FRO_TOL_F8 if f8 else FRO_TOL_F32, what=what)
+    return check_rounded(g, o, T, K, what=what, fro_tol=FRO_TOL_F8 if f8 else None)

@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports what include/tmm.h declares, and rejects bad
+arguments on the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tmm.h")
+
+
+@pytest.fixture(scope="module")
+def tmm():
+    import tiled_matrix_multiplication_amd as t
+    return t
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tmm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(
+        ["tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemv", "tmm_status_string", "tmm_version"])
+
+
+def test_library_exports_every_declared_symbol(tmm):
+    raw = ctypes.CDLL(tmm.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert set(tmm.EXPORTS) == set(declared_functions())
+
+
+def test_version_and_status_strings(tmm):
+    assert tmm.tmm_version() == 10000
+    for code in range(-8, 1):
+        s = tmm.tmm_status_string(code)
+        assert s and s != "unknown status code", code
+    assert tmm.tmm_status_string(-99) == "unknown status code"
+
+
+FAKE = ctypes.c_void_p(0x100000)     # never dereferenced: every call below fails validation
+FAKE2 = ctypes.c_void_p(0x200000)
+FAKE3 = ctypes.c_void_p(0x300000)
+
+
+def gemm(tmm, M=64, N=64, K=64, ab=1, c=0, tb=0, A=FAKE, lda=None, B=FAKE2, ldb=None, C=FAKE3,
+         ldc=None, bias=None, sa=1.0, sb=1.0):
+    lda = K if lda is None else lda
+    ldb = (K if tb else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return tmm.lib.tmm_gemm(M, N, K, ab, c, tb, A, lda, B, ldb, C, ldc, bias, sa, sb, None)
+
+
+def batched(tmm, M=64, N=64, K=64, sA=4096, sB=4096, sC=4096, batch=2, **kw):
+    return tmm.lib.tmm_gemm_strided_batched(M, N, K, kw.get("ab", 1), kw.get("c", 0), 0, FAKE, K, sA,
+                                            FAKE2, N, sB, kw.get("C", FAKE3), N, sC, batch, None,
+                                            1.0, 1.0, None)
+
+
+def test_dimension_errors(tmm):
+    assert gemm(tmm, M=-1) == -1
+    assert gemm(tmm, N=-5) == -1
+    assert gemm(tmm, K=-1, lda=1) == -1
+    assert batched(tmm, batch=-1) == -1
+
+
+def test_leading_dimension_errors(tmm):
+    assert gemm(tmm, lda=63) == -2
+    assert gemm(tmm, ldb=63) == -2
+    assert gemm(tmm, tb=1, ldb=63) == -2          # NT: ldb >= K
+    assert gemm(tmm, ldc=10) == -2
+    assert gemm(tmm, K=0, lda=0) == -2            # ld must be at least 1
+
+
+def test_type_errors(tmm):
+    assert gemm(tmm, ab=7) == -4
+    assert gemm(tmm, ab=0, c=1) == -4             # f32 -> bf16 not offered
+    assert gemm(tmm, ab=1, c=2) == -4             # bf16 -> f16
+    assert gemm(tmm, ab=2, c=1) == -4             # f16 -> bf16
+    assert gemm(tmm, ab=3, c=2) == -4             # fp8 -> f16
+    assert tmm.lib.tmm_gemv(8, 8, 3, 1, FAKE, 8, FAKE2, FAKE3, None, None) == -4   # no fp8 GEMV
+
+
+def test_scale_errors(tmm):
+    assert gemm(tmm, sa=2.0) == -5                # scales only for fp8
+    assert gemm(tmm, ab=3, c=1, sa=float("nan")) == -5
+    assert gemm(tmm, ab=3, c=1, sb=float("inf")) == -5
+
+
+def test_null_and_alignment_errors(tmm):
+    assert gemm(tmm, C=None) == -3
+    assert gemm(tmm, A=None) == -3
+    assert gemm(tmm, B=None) == -3
+    assert gemm(tmm, A=ctypes.c_void_p(0x100001)) == -7     # bf16 at an odd address
+    assert gemm(tmm, c=0, C=ctypes.c_void_p(0x300002)) == -7  # fp32 output at 2 mod 4
+    assert gemm(tmm, bias=ctypes.c_void_p(0x400002)) == -7
+    assert tmm.lib.tmm_gemv(8, 8, 1, 1, None, 8, FAKE2, FAKE3, None, None) == -3
+    assert tmm.lib.tmm_gemv(8, 8, 1, 1, FAKE, 4, FAKE2, FAKE3, None, None) == -2
+
+
+def test_batch_stride_errors(tmm):
+    assert batched(tmm, sC=64 * 64 - 1) == -6     # C matrices would overlap
+    assert batched(tmm, sA=-1) == -6
+    # zero A/B strides (one operand for every problem) pass the stride check and
+    # reach the NULL check behind it; no call here may pass validation
+    assert batched(tmm, sC=64 * 64, sA=0, sB=0, C=None) == -3
+
+
+def test_quick_returns_enqueue_nothing(tmm):
+    # M == 0, N == 0, batch == 0: success without touching any pointer or the GPU
+    assert gemm(tmm, M=0, A=None, B=None, C=None) == 0
+    assert gemm(tmm, N=0, A=None, B=None, C=None, ldb=1, ldc=1) == 0
+    assert batched(tmm, batch=0, C=None) == 0
+    assert tmm.lib.tmm_gemv(0, 16, 1, 1, None, 16, None, None, None, None) == 0
+
+
+def test_binding_rejects_host_tensors(tmm):
+    import torch
+    a = torch.zeros(4, 4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tmm.tmm_gemm(a, a, torch.zeros(4, 4))

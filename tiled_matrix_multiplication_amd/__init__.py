@@ -1,0 +1,163 @@
+"""Python binding of libtmm.so (tiled GEMM / GEMV for MI355X, gfx950).
+
+Argument marshalling only: each function takes torch tensors that already
+live on the GPU, reads their shapes, strides, element types and data
+pointers, and calls the C entry point of the same name (see
+``include/tmm.h``) on the current torch stream (or the given one).  All
+arithmetic happens in the library's HIP kernels.  There is no fallback: if
+``libtmm.so`` is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtmm.so")
+
+TMM_F32, TMM_BF16, TMM_F16, TMM_F8E4M3 = 0, 1, 2, 3
+
+STATUS = {
+    0: "TMM_OK", -1: "TMM_ERR_DIM", -2: "TMM_ERR_LD", -3: "TMM_ERR_NULL", -4: "TMM_ERR_DTYPE",
+    -5: "TMM_ERR_SCALE", -6: "TMM_ERR_STRIDE", -7: "TMM_ERR_ALIGN", -8: "TMM_ERR_LAUNCH",
+}
+
+EXPORTS = ("tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemv", "tmm_status_string", "tmm_version")
+
+_DTYPE = {torch.float32: TMM_F32, torch.bfloat16: TMM_BF16, torch.float16: TMM_F16,
+          torch.float8_e4m3fn: TMM_F8E4M3}
+
+
+class TmmError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn}: {STATUS.get(code, code)} ({tmm_status_string(code)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m tiled_matrix_multiplication_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, ci, cf = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.tmm_gemm.argtypes = [i64, i64, i64, ci, ci, ci, vp, i64, vp, i64, vp, i64, vp, cf, cf, vp]
+    lib.tmm_gemm_strided_batched.argtypes = [i64, i64, i64, ci, ci, ci, vp, i64, i64, vp, i64, i64,
+                                             vp, i64, i64, i64, vp, cf, cf, vp]
+    lib.tmm_gemv.argtypes = [i64, i64, ci, ci, vp, i64, vp, vp, vp, vp]
+    lib.tmm_status_string.argtypes = [ci]
+    lib.tmm_status_string.restype = ctypes.c_char_p
+    lib.tmm_version.argtypes = []
+    for f in (lib.tmm_gemm, lib.tmm_gemm_strided_batched, lib.tmm_gemv, lib.tmm_version):
+        f.restype = ci
+    return lib
+
+
+lib = _load()
+
+
+def tmm_status_string(code: int) -> str:
+    return lib.tmm_status_string(int(code)).decode()
+
+
+def tmm_version() -> int:
+    return int(lib.tmm_version())
+
+
+# ---------------------------------------------------------------- marshalling
+
+
+def _dtype(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported element type {t.dtype}") from None
+
+
+def _on_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+
+
+def _ld(t: torch.Tensor) -> int:
+    """Leading dimension of a row-major 2-D view (rows contiguous)."""
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous (stride 1)")
+    return max(int(t.stride(-2)) if t.shape[-2] > 1 else int(t.shape[-1]), 1)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise TmmError(fn, rc)
+
+
+def tmm_gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, bias: torch.Tensor | None = None,
+             trans_b: bool = False, scale_a: float = 1.0, scale_b: float = 1.0, stream=None):
+    """C = scale_a*scale_b * A . op(B) (+ bias).  A (M,K); B (K,N) or (N,K) with trans_b; C (M,N)."""
+    _on_gpu(A, B, C, bias)
+    M, K = A.shape
+    N = B.shape[0] if trans_b else B.shape[1]
+    if (B.shape[1] if trans_b else B.shape[0]) != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    if B.dtype != A.dtype:
+        raise TypeError("A and B must have the same element type")
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (N,) or bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous float32 vector of N entries")
+    rc = lib.tmm_gemm(M, N, K, _dtype(A), _dtype(C), int(bool(trans_b)), _ptr(A), _ld(A), _ptr(B),
+                      _ld(B), _ptr(C), _ld(C), _ptr(bias), float(scale_a), float(scale_b),
+                      ctypes.c_void_p(_stream(stream)))
+    _check("tmm_gemm", rc)
+    return C
+
+
+def tmm_gemm_strided_batched(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                             bias: torch.Tensor | None = None, trans_b: bool = False,
+                             scale_a: float = 1.0, scale_b: float = 1.0, stream=None):
+    """C[z] = scale_a*scale_b * A[z] . op(B[z]) (+ bias) for 3-D tensors (batch, rows, cols)."""
+    _on_gpu(A, B, C, bias)
+    Z, M, K = A.shape
+    N = B.shape[1] if trans_b else B.shape[2]
+    if B.shape[0] != Z or C.shape[0] != Z or tuple(C.shape[1:]) != (M, N) or \
+            (B.shape[2] if trans_b else B.shape[1]) != K:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    if B.dtype != A.dtype:
+        raise TypeError("A and B must have the same element type")
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (N,) or bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous float32 vector of N entries")
+    rc = lib.tmm_gemm_strided_batched(
+        M, N, K, _dtype(A), _dtype(C), int(bool(trans_b)), _ptr(A), _ld(A), int(A.stride(0)),
+        _ptr(B), _ld(B), int(B.stride(0)), _ptr(C), _ld(C), int(C.stride(0)), Z, _ptr(bias),
+        float(scale_a), float(scale_b), ctypes.c_void_p(_stream(stream)))
+    _check("tmm_gemm_strided_batched", rc)
+    return C
+
+
+def tmm_gemv(W: torch.Tensor, x: torch.Tensor, y: torch.Tensor, bias: torch.Tensor | None = None,
+             stream=None):
+    """y = W . x (+ bias).  W (N, K) row-major, x (K,), y (N,)."""
+    _on_gpu(W, x, y, bias)
+    N, K = W.shape
+    if tuple(x.shape) != (K,) or tuple(y.shape) != (N,):
+        raise ValueError(f"shape mismatch: W {tuple(W.shape)}, x {tuple(x.shape)}, y {tuple(y.shape)}")
+    if x.dtype != W.dtype:
+        raise TypeError("W and x must have the same element type")
+    if (K > 1 and x.stride(0) != 1) or (N > 1 and y.stride(0) != 1):
+        raise ValueError("x and y must be contiguous")
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (N,) or bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous float32 vector of N entries")
+    rc = lib.tmm_gemv(N, K, _dtype(W), _dtype(y), _ptr(W), _ld(W), _ptr(x), _ptr(y), _ptr(bias),
+                      ctypes.c_void_p(_stream(stream)))
+    _check("tmm_gemv", rc)
+    return y

@@ -1,0 +1,205 @@
+// Matrix-vector product y = W . x (+ bias) and the K == 0 fill of the GEMM.
+//
+// The GEMV is the batch-1 linear layer: every weight is used once, so the
+// kernel is a stream over W and its speed is HBM bandwidth, not arithmetic
+// (Level-2 BLAS is memory-bound: "GEMM to FlashAttention" page, BLAS levels
+// list and the batch-1 intensity case of its analyze_matmul_intensity
+// listing; CMU 15-418 Lecture 27 notes, section 7, question 1: about one
+// flop per weight byte).  Matrix instructions would not help; the design
+// goal is enough bytes in flight:
+//   * one wave (64 lanes) owns R consecutive rows; each lane issues all of
+//     its 16-byte loads of those rows before using any (8 loads per row for
+//     K = 4096 bf16), so a CU keeps ~128 KiB of W in flight;
+//   * lane l takes chunks l, l+64, ... of a row: every load instruction of a
+//     wave covers 1 KiB of contiguous weights;
+//   * x is loaded once per wave into registers and reused for the R rows;
+//   * fp32 FMAs, then a 64-lane butterfly sum (the wave analogue of the
+//     warp-shuffle reduction in the Lecture 27 fused-attention listing),
+//     bias, one round-to-nearest-even store.
+#include "tmm_internal.h"
+
+namespace tmm {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <int F> struct Bytes;
+template <> struct Bytes<kF32> { static constexpr int value = 4; };
+template <> struct Bytes<kBF16> { static constexpr int value = 2; };
+template <> struct Bytes<kF16> { static constexpr int value = 2; };
+
+__device__ __forceinline__ float lo_f16(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float hi_f16(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// acc += sum over the elements of a 16-byte chunk pair (w, x).
+template <int F>
+__device__ __forceinline__ float dot_chunk(float acc, i32x4 w, i32x4 x) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t a = (uint32_t)w[q], b = (uint32_t)x[q];
+    if constexpr (F == kBF16) {
+      acc = __builtin_fmaf(lo_bf16(a), lo_bf16(b), acc);
+      acc = __builtin_fmaf(hi_bf16(a), hi_bf16(b), acc);
+    } else if constexpr (F == kF16) {
+      acc = __builtin_fmaf(lo_f16(a), lo_f16(b), acc);
+      acc = __builtin_fmaf(hi_f16(a), hi_f16(b), acc);
+    } else {
+      acc = __builtin_fmaf(__uint_as_float(a), __uint_as_float(b), acc);
+    }
+  }
+  return acc;
+}
+
+template <int F>
+__device__ __forceinline__ float load_elem(const char *p, int64_t idx) {
+  if constexpr (F == kBF16) return __uint_as_float((uint32_t)((const uint16_t *)p)[idx] << 16);
+  else if constexpr (F == kF16) return (float)((const _Float16 *)p)[idx];
+  else return ((const float *)p)[idx];
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int YT>
+__device__ __forceinline__ void put(void *y, int64_t i, float v) {
+  if constexpr (YT == kF32) ((float *)y)[i] = v;
+  else if constexpr (YT == kBF16) ((uint16_t *)y)[i] = to_bf16(v);
+  else ((uint16_t *)y)[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+constexpr int kWaves = 4;  // waves per workgroup
+constexpr int kUnroll = 8; // 16-byte chunks per lane per row in one pass
+
+// 16-byte path: K*E is a multiple of 16 and W, x, ldw are 16-byte aligned.
+template <int WT, int YT, int R>
+__global__ __launch_bounds__(64 * kWaves) void gemv_vec_kernel(GemvParams p) {
+  constexpr int E = Bytes<WT>::value;
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;
+  if (row0 >= p.N) return;
+  const int64_t nchunks = p.K * E / 16;
+  const char *W = (const char *)p.W;
+  const char *x = (const char *)p.x;
+  const char *wrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t rr = row0 + r < p.N ? row0 + r : p.N - 1;
+    wrow[r] = W + rr * p.ldw * E;
+  }
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+
+  for (int64_t c0 = 0; c0 < nchunks; c0 += 64 * kUnroll) {
+    i32x4 xv[kUnroll], wv[R][kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t cc = c0 + u * 64 + lane;
+      const bool ok = cc < nchunks;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        wv[r][u] = ok ? *(const i32x4 *)(wrow[r] + cc * 16) : i32x4{0, 0, 0, 0};
+      xv[u] = ok ? *(const i32x4 *)(x + cc * 16) : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = dot_chunk<WT>(acc[r], wv[r][u], xv[u]);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float s = wave_sum(acc[r]);
+    if (lane == r && row0 + r < p.N) put<YT>(p.y, row0 + r, s + (p.bias ? p.bias[row0 + r] : 0.f));
+  }
+}
+
+// Element path for any alignment.
+template <int WT, int YT>
+__global__ __launch_bounds__(64 * kWaves) void gemv_elem_kernel(GemvParams p) {
+  constexpr int E = Bytes<WT>::value;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= p.N) return;
+  const char *w = (const char *)p.W + row * p.ldw * E;
+  float acc = 0.f;
+  for (int64_t k = lane; k < p.K; k += 64)
+    acc = __builtin_fmaf(load_elem<WT>(w, k), load_elem<WT>((const char *)p.x, k), acc);
+  const float s = wave_sum(acc);
+  if (lane == 0) put<YT>(p.y, row, s + (p.bias ? p.bias[row] : 0.f));
+}
+
+constexpr int kRows = 2;  // rows per wave on the 16-byte path
+
+template <int WT, int YT>
+hipError_t launch_typed(bool vec, const GemvParams &p, hipStream_t stream) {
+  if (vec) {
+    const int64_t waves = (p.N + kRows - 1) / kRows;
+    const unsigned blocks = (unsigned)((waves + kWaves - 1) / kWaves);
+    hipLaunchKernelGGL((gemv_vec_kernel<WT, YT, kRows>), dim3(blocks), dim3(64 * kWaves), 0,
+                       stream, p);
+  } else {
+    const unsigned blocks = (unsigned)((p.N + kWaves - 1) / kWaves);
+    hipLaunchKernelGGL((gemv_elem_kernel<WT, YT>), dim3(blocks), dim3(64 * kWaves), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+// ---- K == 0 fill for the GEMM: C = bias (or 0)
+template <int CT>
+__global__ __launch_bounds__(256) void fill_kernel(GemmParams p) {
+  const int64_t per = p.M * p.N;
+  const int64_t total = per * p.batch;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t z = t / per;
+    const int64_t rem = t - z * per;
+    const int64_t row = rem / p.N, col = rem - row * p.N;
+    const float v = p.bias ? p.bias[col] : 0.f;
+    const int64_t idx = z * p.strideC + row * p.ldc + col;
+    put<CT>(p.C, idx, v);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv(Fmt w, Fmt y, bool vec, const GemvParams &p, hipStream_t stream) {
+  if (w == kF32) return launch_typed<kF32, kF32>(vec, p, stream);
+  if (w == kBF16)
+    return y == kF32 ? launch_typed<kBF16, kF32>(vec, p, stream)
+                     : launch_typed<kBF16, kBF16>(vec, p, stream);
+  if (w == kF16)
+    return y == kF32 ? launch_typed<kF16, kF32>(vec, p, stream)
+                     : launch_typed<kF16, kF16>(vec, p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fill(Fmt c, const GemmParams &p, hipStream_t stream) {
+  const int64_t total = p.M * p.N * p.batch;
+  const int64_t want = (total + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 65536 ? (want > 0 ? want : 1) : 65536);
+  switch (c) {
+    case kF32: hipLaunchKernelGGL(fill_kernel<kF32>, dim3(blocks), dim3(256), 0, stream, p); break;
+    case kBF16: hipLaunchKernelGGL(fill_kernel<kBF16>, dim3(blocks), dim3(256), 0, stream, p); break;
+    case kF16: hipLaunchKernelGGL(fill_kernel<kF16>, dim3(blocks), dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tmm

@@ -1,0 +1,244 @@
+// C-ABI entry points of libtmm.so: argument checks, quick returns, and the
+// choice of kernel by shape, type and alignment.  Declarations and the full
+// contract are in include/tmm.h.
+//
+// Every check runs on the host before any HIP call, so a rejected call has
+// no side effect and the checks are testable on a machine without a GPU.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/tmm.h"
+#include "tmm_internal.h"
+
+namespace {
+
+using tmm::Fmt;
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+int elem_bytes(int t) { return t == TMM_F32 ? 4 : t == TMM_F8E4M3 ? 1 : 2; }
+
+bool known_type(int t) { return t >= TMM_F32 && t <= TMM_F8E4M3; }
+
+// ab -> c pairs the kernels implement.
+bool pair_ok(int ab, int c) {
+  switch (ab) {
+    case TMM_F32: return c == TMM_F32;
+    case TMM_BF16: return c == TMM_F32 || c == TMM_BF16;
+    case TMM_F16: return c == TMM_F32 || c == TMM_F16;
+    case TMM_F8E4M3: return c == TMM_F32 || c == TMM_BF16;
+    default: return false;
+  }
+}
+
+bool aligned(const void *p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
+
+int64_t max1(int64_t v) { return v > 1 ? v : 1; }
+
+// Common checks of tmm_gemm and tmm_gemm_strided_batched.  Returns TMM_OK
+// and sets *quick when nothing is to be launched.
+int check_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const void *A,
+               int64_t lda, int64_t sA, const void *B, int64_t ldb, int64_t sB, const void *C,
+               int64_t ldc, int64_t sC, int64_t batch, const float *bias, float scale_a,
+               float scale_b, bool *quick) {
+  *quick = false;
+  if (M < 0 || N < 0 || K < 0 || batch < 0) return TMM_ERR_DIM;
+  if (!known_type(ab) || !known_type(c) || !pair_ok(ab, c)) return TMM_ERR_DTYPE;
+  if (!isfinite(scale_a) || !isfinite(scale_b)) return TMM_ERR_SCALE;
+  if (ab != TMM_F8E4M3 && (scale_a != 1.0f || scale_b != 1.0f)) return TMM_ERR_SCALE;
+  if (lda < max1(K) || ldb < max1(trans_b ? K : N) || ldc < max1(N)) return TMM_ERR_LD;
+  if (sA < 0 || sB < 0 || sC < 0) return TMM_ERR_STRIDE;
+  if (M == 0 || N == 0 || batch == 0) {
+    *quick = true;
+    return TMM_OK;
+  }
+  if (batch > 1 && sC < (M - 1) * ldc + N) return TMM_ERR_STRIDE;
+  if (C == nullptr) return TMM_ERR_NULL;
+  if (K > 0 && (A == nullptr || B == nullptr)) return TMM_ERR_NULL;
+  const int e = elem_bytes(ab);
+  if (!aligned(C, elem_bytes(c)) || (bias && !aligned(bias, 4))) return TMM_ERR_ALIGN;
+  if (K > 0 && (!aligned(A, e) || !aligned(B, e))) return TMM_ERR_ALIGN;
+  // The grid has one workgroup per 128x128 tile or larger per problem.
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  if (tiles > (int64_t)0x7fffffff / batch) return TMM_ERR_DIM;
+  return TMM_OK;
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// TMM_FORCE_TILE = "256x256" | "256x128" | "128x128" pins the tile shape
+// (for measurements); anything else leaves the choice to pick_tile.
+int forced_tile() {
+  static int forced = -2;
+  if (forced == -2) {
+    const char *s = getenv("TMM_FORCE_TILE");
+    forced = -1;
+    if (s) {
+      if (!strcmp(s, "256x256")) forced = tmm::kTile256x256;
+      else if (!strcmp(s, "256x128")) forced = tmm::kTile256x128;
+      else if (!strcmp(s, "128x128")) forced = tmm::kTile128x128;
+    }
+  }
+  return forced;
+}
+
+// Tile shape with the least estimated time: rounds of `cus` concurrent
+// tiles times the work of one tile divided by the shape's relative MFMA
+// efficiency (bigger tiles reuse each loaded byte more).
+tmm::Tile pick_tile(int64_t M, int64_t N, int64_t batch, int ab) {
+  const int f = forced_tile();
+  if (f >= 0) return (tmm::Tile)f;
+  if (ab == TMM_F32) return tmm::kTile128x128;
+  const int cus = cu_count();
+  const double eff[tmm::kNumTiles] = {1.0, 0.85, 0.65};
+  tmm::Tile best = tmm::kTile128x128;
+  double best_cost = 1e300;
+  for (int t = 0; t < tmm::kNumTiles; ++t) {
+    const int bm = tmm::tile_bm((tmm::Tile)t), bn = tmm::tile_bn((tmm::Tile)t);
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * batch;
+    const int64_t rounds = (tiles + cus - 1) / cus;
+    const double cost = (double)rounds * bm * bn / eff[t];
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = (tmm::Tile)t;
+    }
+  }
+  return best;
+}
+
+hipError_t dispatch_gemm(int ab, int c, bool trans_b, tmm::Tile tile, bool vec,
+                         const tmm::GemmParams &p, hipStream_t s) {
+  switch (ab) {
+    case TMM_F32: return tmm::launch_gemm_f32((Fmt)c, trans_b, tile, vec, p, s);
+    case TMM_BF16: return tmm::launch_gemm_bf16((Fmt)c, trans_b, tile, vec, p, s);
+    case TMM_F16: return tmm::launch_gemm_f16((Fmt)c, trans_b, tile, vec, p, s);
+    default: return tmm::launch_gemm_f8((Fmt)c, trans_b, tile, vec, p, s);
+  }
+}
+
+int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const void *A,
+             int64_t lda, int64_t sA, const void *B, int64_t ldb, int64_t sB, void *C, int64_t ldc,
+             int64_t sC, int64_t batch, const float *bias, float scale_a, float scale_b,
+             hipStream_t stream) {
+  bool quick = false;
+  const int rc = check_gemm(M, N, K, ab, c, trans_b, A, lda, sA, B, ldb, sB, C, ldc, sC, batch,
+                            bias, scale_a, scale_b, &quick);
+  if (rc != TMM_OK || quick) return rc;
+
+  tmm::GemmParams p;
+  p.M = M; p.N = N; p.K = K;
+  p.A = A; p.lda = lda; p.strideA = sA;
+  p.B = B; p.ldb = ldb; p.strideB = sB;
+  p.C = C; p.ldc = ldc; p.strideC = sC;
+  p.bias = bias;
+  p.scale = scale_a * scale_b;
+  p.batch = batch;
+
+  hipError_t err;
+  if (K == 0) {
+    err = tmm::launch_fill((Fmt)c, p, stream);
+  } else if (M == 1 && batch == 1 && trans_b && ab != TMM_F8E4M3) {
+    // y = W . x with W = B (N x K): the memory-bound matrix-vector path.
+    tmm::GemvParams g;
+    g.N = N; g.K = K; g.W = B; g.ldw = ldb; g.x = A; g.y = C; g.bias = bias;
+    const int e = elem_bytes(ab);
+    const bool vec = aligned(B, 16) && aligned(A, 16) && (ldb * e) % 16 == 0 && (K * e) % 16 == 0;
+    err = tmm::launch_gemv((Fmt)ab, (Fmt)c, vec, g, stream);
+  } else {
+    const int e = elem_bytes(ab);
+    // 16-byte loads need every row of A and B to start on a 16-byte boundary,
+    // and the batch strides to keep it so.
+    const bool vec = aligned(A, 16) && aligned(B, 16) && (lda * e) % 16 == 0 &&
+                     (ldb * e) % 16 == 0 && (batch == 1 || ((sA * e) % 16 == 0 && (sB * e) % 16 == 0));
+    const tmm::Tile tile = vec ? pick_tile(M, N, batch, ab) : tmm::kTile128x128;
+    err = dispatch_gemm(ab, c, trans_b != 0, tile, vec, p, stream);
+  }
+  return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tmm_gemm(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type, tmm_dtype c_type, int trans_b,
+             const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
+             const float *bias, float scale_a, float scale_b, hipStream_t stream) {
+  return run_gemm(M, N, K, ab_type, c_type, trans_b, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, bias,
+                  scale_a, scale_b, stream);
+}
+
+int tmm_gemm_strided_batched(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type,
+                             tmm_dtype c_type, int trans_b, const void *A, int64_t lda,
+                             int64_t strideA, const void *B, int64_t ldb, int64_t strideB, void *C,
+                             int64_t ldc, int64_t strideC, int64_t batch, const float *bias,
+                             float scale_a, float scale_b, hipStream_t stream) {
+  return run_gemm(M, N, K, ab_type, c_type, trans_b, A, lda, strideA, B, ldb, strideB, C, ldc,
+                  strideC, batch, bias, scale_a, scale_b, stream);
+}
+
+int tmm_gemv(int64_t N, int64_t K, tmm_dtype w_type, tmm_dtype y_type, const void *W,
+             int64_t ldw, const void *x, void *y, const float *bias, hipStream_t stream) {
+  if (N < 0 || K < 0) return TMM_ERR_DIM;
+  if (!known_type(w_type) || !known_type(y_type) || w_type == TMM_F8E4M3 ||
+      !pair_ok(w_type, y_type))
+    return TMM_ERR_DTYPE;
+  if (ldw < max1(K)) return TMM_ERR_LD;
+  if (N == 0) return TMM_OK;
+  if (y == nullptr) return TMM_ERR_NULL;
+  if (K > 0 && (W == nullptr || x == nullptr)) return TMM_ERR_NULL;
+  const int e = elem_bytes(w_type);
+  if (!aligned(y, elem_bytes(y_type)) || (bias && !aligned(bias, 4))) return TMM_ERR_ALIGN;
+  if (K > 0 && (!aligned(W, e) || !aligned(x, e))) return TMM_ERR_ALIGN;
+  if (N > (int64_t)0x7fffffff) return TMM_ERR_DIM;
+
+  hipError_t err;
+  if (K == 0) {
+    tmm::GemmParams p;
+    memset(&p, 0, sizeof p);
+    p.M = 1; p.N = N; p.K = 0; p.C = y; p.ldc = N; p.bias = bias; p.batch = 1; p.scale = 1.f;
+    err = tmm::launch_fill((Fmt)y_type, p, stream);
+  } else {
+    tmm::GemvParams g;
+    g.N = N; g.K = K; g.W = W; g.ldw = ldw; g.x = x; g.y = y; g.bias = bias;
+    const bool vec = aligned(W, 16) && aligned(x, 16) && (ldw * e) % 16 == 0 && (K * e) % 16 == 0;
+    err = tmm::launch_gemv((Fmt)w_type, (Fmt)y_type, vec, g, stream);
+  }
+  return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
+}
+
+const char *tmm_status_string(int status) {
+  switch (status) {
+    case TMM_OK: return "success";
+    case TMM_ERR_DIM: return "negative or too large dimension or batch";
+    case TMM_ERR_LD: return "leading dimension smaller than the row length";
+    case TMM_ERR_NULL: return "null pointer for an operand with non-zero extent";
+    case TMM_ERR_DTYPE: return "unsupported element type or type combination";
+    case TMM_ERR_SCALE: return "scale must be finite, and 1 unless the inputs are fp8";
+    case TMM_ERR_STRIDE: return "negative batch stride or overlapping output matrices";
+    case TMM_ERR_ALIGN: return "pointer not aligned to its element size";
+    case TMM_ERR_LAUNCH: return "HIP reported an error at kernel launch";
+    default: return "unknown status code";
+  }
+}
+
+int tmm_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal interface between the C-ABI dispatch (tmm_api.hip) and the
+// kernel translation units.  Nothing here crosses the library boundary.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tmm {
+
+// Element formats, same numbering as tmm_dtype in include/tmm.h.
+enum Fmt : int { kF32 = 0, kBF16 = 1, kF16 = 2, kF8 = 3 };
+
+// Workgroup tile shapes of the MFMA GEMM kernel.
+enum Tile : int { kTile256x256 = 0, kTile256x128 = 1, kTile128x128 = 2, kNumTiles = 3 };
+
+struct GemmParams {
+  int64_t M, N, K;
+  const void *A;
+  int64_t lda, strideA;
+  const void *B;
+  int64_t ldb, strideB;
+  void *C;
+  int64_t ldc, strideC;
+  const float *bias;
+  float scale;      // scale_a * scale_b (1 unless fp8)
+  int64_t batch;
+};
+
+// Rows/columns of a workgroup tile.
+inline int tile_bm(Tile t) { return t == kTile128x128 ? 128 : 256; }
+inline int tile_bn(Tile t) { return t == kTile256x256 ? 256 : 128; }
+
+// Launch the tiled MFMA GEMM for one input type with the given tile shape.
+// `vec` selects the 16-byte-load path (every operand row 16-byte aligned);
+// otherwise element loads are used (128x128 tiles).  Returns hipSuccess or
+// the launch error.
+hipError_t launch_gemm_f32(Fmt c, bool trans_b, Tile tile, bool vec, const GemmParams &p,
+                           hipStream_t stream);
+hipError_t launch_gemm_bf16(Fmt c, bool trans_b, Tile tile, bool vec, const GemmParams &p,
+                            hipStream_t stream);
+hipError_t launch_gemm_f16(Fmt c, bool trans_b, Tile tile, bool vec, const GemmParams &p,
+                           hipStream_t stream);
+hipError_t launch_gemm_f8(Fmt c, bool trans_b, Tile tile, bool vec, const GemmParams &p,
+                          hipStream_t stream);
+
+// C = bias broadcast (or 0) for the K == 0 empty sum.
+hipError_t launch_fill(Fmt c, const GemmParams &p, hipStream_t stream);
+
+struct GemvParams {
+  int64_t N, K;
+  const void *W;
+  int64_t ldw;
+  const void *x;
+  void *y;
+  const float *bias;
+};
+
+hipError_t launch_gemv(Fmt w, Fmt y, bool vec, const GemvParams &p, hipStream_t stream);
+
+}  // namespace tmm
