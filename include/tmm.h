@@ -57,6 +57,11 @@
  * enqueues nothing, prints nothing and never exits.  TMM_ERR_LAUNCH reports a
  * HIP error seen right after the launch.
  *
+ * Size limits: A and B of one problem must each span less than 4 GiB
+ * (the kernels address them with 32-bit byte offsets), and the number of
+ * 128 x 128 output tiles times batch must stay below 2^31; otherwise the
+ * call returns TMM_ERR_DIM.
+ *
  * Quick returns: M == 0, N == 0 or batch == 0 enqueue nothing and return 0
  * (pointers are not checked then).  K == 0 is the empty sum: C = bias (or 0).
  */
@@ -80,7 +85,7 @@ typedef enum tmm_dtype {
 
 enum tmm_status {
   TMM_OK = 0,
-  TMM_ERR_DIM = -1,    /* M, N, K or batch negative                          */
+  TMM_ERR_DIM = -1,    /* M, N, K or batch negative, or a problem too large  */
   TMM_ERR_LD = -2,     /* a leading dimension below its row length (or < 1)  */
   TMM_ERR_NULL = -3,   /* NULL pointer for an operand with non-zero extent    */
   TMM_ERR_DTYPE = -4,  /* unknown type or a type pair not in the table above  */

@@ -123,3 +123,8 @@ def test_binding_rejects_host_tensors(tmm):
     a = torch.zeros(4, 4, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         tmm.tmm_gemm(a, a, torch.zeros(4, 4))
+
+
+def test_operand_span_limit(tmm):
+    # 65536 x 32769 bf16 = 4 GiB + 128 KiB: rejected before any HIP call
+    assert gemm(tmm, M=65536, N=64, K=32769) == -1

@@ -39,7 +39,7 @@ class TmmError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m tiled_matrix_multiplication_amd.build`")
+            f"{LIB_PATH} is missing: build it with `python tiled_matrix_multiplication_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, ci, cf = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.tmm_gemm.argtypes = [i64, i64, i64, ci, ci, ci, vp, i64, vp, i64, vp, i64, vp, cf, cf, vp]

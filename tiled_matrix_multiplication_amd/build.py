@@ -2,7 +2,8 @@
 
 Each csrc/*.hip file is compiled to an object under _build/ (in parallel),
 then linked into tiled_matrix_multiplication_amd/libtmm.so.  Run as
-``python -m tiled_matrix_multiplication_amd.build``.
+``python tiled_matrix_multiplication_amd/build.py`` (not through the package,
+whose import loads the library this script replaces).
 """
 from __future__ import annotations
 

@@ -14,7 +14,7 @@
 //   * LDS rows are 128 bytes (one K-step of any element type: 64 bf16/fp16,
 //     128 fp8, 32 fp32) made of eight 16-byte chunks; chunk c of row r is
 //     stored at chunk position c ^ swz(r), so the 16-byte fragment reads of
-//     32 consecutive rows and the row-wise writes hit distinct banks (the
+//     consecutive rows and the transposing writes hit distinct banks (the
 //     swizzle-against-bank-conflicts idea of the MLC GPU-programming
 //     tutorial reviewed on devtrends.cc).
 //   * Two LDS stages: the global loads of K-step k+1 are issued before the
@@ -57,7 +57,6 @@ template <> struct FmtBytes<kF16> { static constexpr int value = 2; };
 template <> struct FmtBytes<kF8> { static constexpr int value = 1; };
 
 constexpr int kRowBytes = 128;  // bytes of one K-step per tile row
-constexpr int kThreads = 256;   // 4 waves
 constexpr int kGroupM = 4;      // tile-rows per ordering group
 
 // ---------------------------------------------------------------- helpers
@@ -65,7 +64,11 @@ constexpr int kGroupM = 4;      // tile-rows per ordering group
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// Chunk swizzle of LDS row `row`: logical chunk c is stored at position
+// c ^ swz(row).  Any 8 consecutive rows, and any 8 rows spaced 8 apart, get 8
+// distinct values, so 16-byte fragment reads of consecutive rows and the NN
+// transpose writes (rows 8 apart per lane) spread over all banks.
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ swz(row)) << 4);
@@ -92,6 +95,13 @@ __device__ __forceinline__ i32x4 load_chunk_elems(const char *p, int nvalid) {
 }
 
 __device__ __forceinline__ i32x4 load16(const char *p) { return *(const i32x4 *)p; }
+
+// 16 bytes per lane from global memory straight into LDS: lane L of the wave
+// writes lds_wave_base + 16 L (gfx950 global_load_lds_dwordx4).  Kept out of
+// lambdas: inside one, hipcc's host pass drops the kernel's launch stub.
+__device__ __forceinline__ void load16_to_lds(const char *g, char *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_wave_base, 16, 0, 0);
+}
 
 // Workgroups go to XCD (id mod 8).  Give XCD x the contiguous tile run
 // [x*n/8, (x+1)*n/8) for the part of the grid that fills whole rounds.
@@ -135,137 +145,153 @@ __device__ __forceinline__ void store_out(char *C, int64_t idx, float v) {
     ((uint16_t *)C)[idx] = f32_to_f16_rne(v);
 }
 
-// One K-step (128 bytes per row) of matrix instructions on fragments read
-// from LDS.  fa[s][i] / fb[s][j] hold, for k-slot s = 0..3, the 16-byte
-// chunk 2s + (lane / 32) of the lane's A row / B column.  A and B use the
-// same slot-to-chunk map, so each instruction pairs equal k indices.
-template <int AB, int FM, int FN>
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[FM][FN], const i32x4 (&fa)[4][FM],
-                                         const i32x4 (&fb)[4][FN]) {
-  if constexpr (AB == kBF16) {
+// Matrix instructions of one K-step (128 bytes of K per row), numbered
+// 0 .. units<AB>(FM, FN) - 1 in issue order.  fa[s][i] / fb[s][j] hold, for
+// k-slot s = 0..3, the 16-byte chunk 2s + (lane / 32) of the lane's A row /
+// B column; A and B use the same slot-to-chunk map, so each instruction
+// pairs equal k indices.
+//   bf16 / fp16: 32x32x16, one slot per instruction, unit = (s, i, j)
+//   fp8 e4m3:    32x32x64, 32 bytes of K per lane = slots 2h and 2h+1,
+//                unit = (h, i, j)
+//   fp32:        32x32x2, one float per lane, a slot holds 4 floats,
+//                unit = (s, t, i, j)
+template <int AB>
+constexpr int units_per_step(int fm, int fn) {
+  return AB == kF8 ? 2 * fm * fn : AB == kF32 ? 16 * fm * fn : 4 * fm * fn;
+}
+
+// Last k-slot whose fragments unit u reads.
+template <int AB>
+constexpr int unit_last_slot(int u, int fm, int fn) {
+  return AB == kF8 ? 2 * (u / (fm * fn)) + 1 : AB == kF32 ? u / (4 * fm * fn) : u / (fm * fn);
+}
+
+template <int AB, int FM, int FN, int U0, int U1>
+__device__ __forceinline__ void mma_units(f32x16 (&acc)[FM][FN], const i32x4 (&fa)[4][FM],
+                                          const i32x4 (&fb)[4][FN]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, fa[s][i]), __builtin_bit_cast(bf16x8, fb[s][j]),
-              acc[i][j], 0, 0, 0);
-  } else if constexpr (AB == kF16) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(f16x8, fa[s][i]), __builtin_bit_cast(f16x8, fb[s][j]),
-              acc[i][j], 0, 0, 0);
-  } else if constexpr (AB == kF8) {
-    // 32x32x64: 32 bytes of K per lane = slots 2h and 2h+1.
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const i32x4 a0 = fa[2 * h][i], a1 = fa[2 * h + 1][i];
-          const i32x4 b0 = fb[2 * h][j], b1 = fb[2 * h + 1][j];
-          const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-          // format code 0 = fp8 E4M3 for both operands; zero scale operands
-          // select the unscaled instruction
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0,
-                                                                       0, 0);
-        }
-  } else {
-    // fp32 32x32x2: one float of K per lane; a slot's chunk holds 4 floats.
-    // Elements are copied to scalars before reinterpretation: hipcc (clang
-    // 22) folds __builtin_bit_cast of a vector-element lvalue to element 0.
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int av = fa[s][i][t], bv = fb[s][j][t];
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(av),
-                                                              __int_as_float(bv), acc[i][j], 0, 0,
-                                                              0);
-          }
+  for (int u = U0; u < U1; ++u) {
+    const int ij = u % (FM * FN);
+    const int i = ij / FN, j = ij % FN;
+    if constexpr (AB == kBF16) {
+      const int s = u / (FM * FN);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[s][i]),
+                                                          __builtin_bit_cast(bf16x8, fb[s][j]),
+                                                          acc[i][j], 0, 0, 0);
+    } else if constexpr (AB == kF16) {
+      const int s = u / (FM * FN);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[s][i]),
+                                                         __builtin_bit_cast(f16x8, fb[s][j]),
+                                                         acc[i][j], 0, 0, 0);
+    } else if constexpr (AB == kF8) {
+      const int h = u / (FM * FN);
+      const i32x4 a0 = fa[2 * h][i], a1 = fa[2 * h + 1][i];
+      const i32x4 b0 = fb[2 * h][j], b1 = fb[2 * h + 1][j];
+      const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      // format code 0 = fp8 E4M3 for both operands; zero scale operands
+      // select the unscaled instruction
+      acc[i][j] =
+          __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
+    } else {
+      // Elements are copied to scalars before reinterpretation: hipcc
+      // (clang 22) folds __builtin_bit_cast of a vector-element lvalue to
+      // element 0.
+      const int st = u / (FM * FN);
+      const int s = st >> 2, t = st & 3;
+      const int av = fa[s][i][t], bv = fb[s][j][t];
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(av), __int_as_float(bv),
+                                                       acc[i][j], 0, 0, 0);
+    }
   }
 }
 
-// Transpose of an (8 k-rows) x (one 16-byte chunk of n) block of an
+// Transpose of an (R k-rows) x (one 16-byte chunk of n) block of an
 // N-contiguous B into LDS rows indexed by n holding K contiguously.
-// in[r] = chunk of row k0 + r.  Column j of the chunk becomes 8 k-values
-// (8*E bytes) stored in LDS row (nrow0 + j) at byte kbyte of the row.
-template <int E>
-__device__ __forceinline__ void store_nn_block(char *lds_b, const i32x4 (&in)[8], int nrow0,
+// in[r] = chunk of row k0 + r.  Column j of the chunk becomes R k-values
+// (R*E bytes) stored in LDS row (nrow0 + j) at byte kbyte of the row.
+template <int E, int R>
+__device__ __forceinline__ void store_nn_block(char *lds_b, const i32x4 (&in)[R], int nrow0,
                                                int kbyte) {
-  if constexpr (E == 2) {
+  constexpr int V = 16 / E;     // columns of the chunk
+  constexpr int W = R * E / 4;  // 32-bit words per column
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      i32x4 o;
+  for (int j = 0; j < V; ++j) {
+    uint32_t o[W];
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        o[w] = (int)__builtin_amdgcn_perm((uint32_t)in[2 * w + 1][j >> 1],
-                                          (uint32_t)in[2 * w][j >> 1], sel);
-      const int row = nrow0 + j;
-      *(i32x4 *)(lds_b + lds_off(row, kbyte >> 4)) = o;
-    }
-  } else if constexpr (E == 1) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int wd = j >> 2, sh = 8 * (j & 3);
-      uint32_t o[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) v |= (((uint32_t)in[4 * h + b][wd] >> sh) & 0xffu) << (8 * b);
-        o[h] = v;
+    for (int w = 0; w < W; ++w) {
+      if constexpr (E == 4) {
+        o[w] = (uint32_t)in[w][j];
+      } else if constexpr (E == 2) {
+        // low or high half of word j/2 of rows 2w and 2w+1
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        o[w] = __builtin_amdgcn_perm((uint32_t)in[2 * w + 1][j >> 1], (uint32_t)in[2 * w][j >> 1], sel);
+      } else {
+        // byte j%4 of word j/4 of rows 4w .. 4w+3 (selector 0x0c gives 0)
+        const uint32_t b = j & 3;
+        const uint32_t sel = b | ((4u + b) << 8) | 0x0c0c0000u;
+        const uint32_t t0 = __builtin_amdgcn_perm((uint32_t)in[4 * w + 1][j >> 2], (uint32_t)in[4 * w][j >> 2], sel);
+        const uint32_t t1 = __builtin_amdgcn_perm((uint32_t)in[4 * w + 3][j >> 2], (uint32_t)in[4 * w + 2][j >> 2], sel);
+        o[w] = __builtin_amdgcn_perm(t1, t0, 0x05040100u);
       }
-      const int row = nrow0 + j;
-      *(i32x2 *)(lds_b + lds_off(row, kbyte >> 4) + (kbyte & 15)) = i32x2{(int)o[0], (int)o[1]};
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = nrow0 + j;
-      const i32x4 o0 = {in[0][j], in[1][j], in[2][j], in[3][j]};
-      const i32x4 o1 = {in[4][j], in[5][j], in[6][j], in[7][j]};
-      *(i32x4 *)(lds_b + lds_off(row, kbyte >> 4)) = o0;
-      *(i32x4 *)(lds_b + lds_off(row, (kbyte >> 4) + 1)) = o1;
+    char *dst = lds_b + lds_off(nrow0 + j, kbyte >> 4) + (kbyte & 15);
+    if constexpr (W == 8) {
+      *(i32x4 *)dst = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+      *(i32x4 *)(lds_b + lds_off(nrow0 + j, (kbyte >> 4) + 1)) = i32x4{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+    } else if constexpr (W == 4) {
+      *(i32x4 *)dst = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+    } else if constexpr (W == 2) {
+      *(i32x2 *)dst = i32x2{(int)o[0], (int)o[1]};
+    } else {
+      *(int *)dst = (int)o[0];
     }
   }
+}
+
+// Scheduling hint: NR (LDS read, MFMA) pairs, then the remaining MFMAs of
+// the region, so the reads issue between matrix instructions.
+template <int NM, int NR>
+__device__ __forceinline__ void interleave_reads() {
+#pragma unroll
+  for (int i = 0; i < NR && i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  if constexpr (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
+  if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
 }
 
 // ---------------------------------------------------------------- kernel
 
-template <int AB, int CT, bool NT, int BM, int BN, bool VEC>
-__global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmParams p) {
+template <int AB, int CT, bool NT, int BM, int BN, int NW, bool VEC>
+__global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
   constexpr int E = FmtBytes<AB>::value;
   constexpr int CE = FmtBytes<CT>::value;
   constexpr int V = 16 / E;           // elements per 16-byte chunk
   constexpr int BK = kRowBytes / E;   // elements of K per step
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int NTH = 64 * NW;          // threads; NW waves as a 2 x (NW/2) grid over the tile
+  constexpr int WGN = NW / 2;
+  constexpr int WTM = BM / 2, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int A_BYTES = BM * kRowBytes;
   constexpr int STAGE = (BM + BN) * kRowBytes;
-  constexpr int AL = BM / 32;                 // A chunks per thread
-  constexpr int BL = NT ? BN / 32 : 8;        // B chunks per thread
-  static_assert(BN <= kThreads, "one N-contiguous B block per thread");
+  constexpr int AL = BM * 8 / NTH;            // A chunks per thread (= direct loads per wave)
+  constexpr int RNN = 8 * BN / NTH;           // NN: k-rows per thread's B block
+  constexpr int BL = NT ? BN * 8 / NTH : RNN; // B chunks per thread
+  constexpr int U = units_per_step<AB>(FM, FN);
+  constexpr int UL = U / 8;                   // units issued after the step's barrier
+  constexpr int PRE = AB == kF8 ? 2 : 1;      // k-slots read before a step starts
+  static_assert(RNN == 4 || RNN == 8, "NN B blocks of 4 or 8 k-rows, one per thread");
+  static_assert(unit_last_slot<AB>(U - UL, FM, FN) == 3, "late units must read slot 3 only");
+  static_assert(unit_last_slot<AB>(U / 4 - 1, FM, FN) < PRE, "phase 0 uses preloaded slots");
 
   __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
   const int g = lane >> 5, l32 = lane & 31;
 
   const int64_t M = p.M, N = p.N, K = p.K;
@@ -281,95 +307,147 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmParams p) {
   const char *A = (const char *)p.A + z * p.strideA * E;
   const char *B = (const char *)p.B + z * p.strideB * E;
 
-  // ---- per-thread global source addresses
-  const int c = tid & 7;  // chunk of a K-contiguous row this thread moves
-  const char *a_src[AL];
+  // Per-lane byte offsets from the problem's base pointers.  The host only
+  // selects this kernel when each operand spans less than 4 GiB, so they fit
+  // 32 bits.
+  // ---- register-path sources (partial K-step, and the element path):
+  // thread moves chunk c of rows (tid / 8) + 32 i
+  const int c = tid & 7;
+  uint32_t a_src[AL];
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
-    const int64_t r = min64(m0 + (tid >> 3) + 32 * i, M - 1);
-    a_src[i] = A + (r * p.lda) * E + c * 16;
+    const int64_t r = min64(m0 + (tid >> 3) + (NTH / 8) * i, M - 1);
+    a_src[i] = (uint32_t)(r * p.lda * E + c * 16);
   }
-  const char *b_src[BL];
+  uint32_t b_src[NT ? BL : 1];
+  uint32_t nn_src = 0;         // NN: offset of row (RNN nn_kb) of this thread's column chunk
   int nb_valid = 0;            // NN: valid columns in this thread's chunk
-  int nn_kb = 0, nn_nc = 0;    // NN: 8-row k block and n chunk of this thread
+  int nn_kb = 0, nn_nc = 0;    // NN: RNN-row k block and n chunk of this thread
+  const uint32_t ldb_bytes = (uint32_t)(p.ldb * E);
   if constexpr (NT) {
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-      const int64_t r = min64(n0 + (tid >> 3) + 32 * i, N - 1);
-      b_src[i] = B + (r * p.ldb) * E + c * 16;
+      const int64_t r = min64(n0 + (tid >> 3) + (NTH / 8) * i, N - 1);
+      b_src[i] = (uint32_t)(r * p.ldb * E + c * 16);
     }
   } else {
-    constexpr int KB = BK / 8;  // 8-row blocks per K-step
-    nn_kb = tid % KB;
-    nn_nc = tid / KB;
+    constexpr int KB = BK / RNN;  // row blocks per K-step; KB * (BN / V) == NTH
+    // column chunk fastest: consecutive lanes read consecutive 16 bytes of a B row
+    nn_nc = tid % (BN / V);
+    nn_kb = tid / (BN / V);
+    static_assert(KB * (BN / V) == NTH, "one NN B block per thread");
     const int64_t ncol = n0 + (int64_t)nn_nc * V;
-    nb_valid = (tid < BN) ? (int)max64(0, min64(V, N - ncol)) : 0;
+    nb_valid = (int)max64(0, min64(V, N - ncol));
     const int64_t ccol = nb_valid > 0 ? ncol : 0;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) b_src[r] = B + ((int64_t)(nn_kb * 8 + r) * p.ldb + ccol) * E;
+    nn_src = (uint32_t)(((int64_t)(nn_kb * RNN) * p.ldb + ccol) * E);
   }
 
-  i32x4 ra[AL], rb[BL];
-
-  // Global -> registers for K-step kt.  `full`: the whole step lies inside K.
-  auto load_step = [&](int64_t kt, bool full) {
-    const int64_t kofs = kt * kRowBytes;  // byte offset along a K-contiguous row
+  // ---- direct global->LDS sources (16-byte path, whole K-steps).  Wave w
+  // fills rows [w*BM/NW, (w+1)*BM/NW) of the A stage, 8 rows per instruction;
+  // lane L lands at position L%8 of row L/8 of its 8-row block, so it loads
+  // logical chunk (L%8) ^ swz(row) of that row.
+  uint32_t a_dl[VEC ? AL : 1];
+  uint32_t b_dl[VEC && NT ? BL : 1];
+  if constexpr (VEC) {
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
-      const char *q = a_src[i] + kofs;
-      if (VEC && full) {
-        ra[i] = load16(q);
-      } else {
-        const int64_t k0 = kt * BK + c * V;
-        const int nv = (int)max64(0, min64(V, K - k0));
-        ra[i] = (VEC && nv == V) ? load16(q) : load_chunk_elems<E>(q, nv);
-      }
+      const int row = wave * (BM / NW) + i * 8 + (lane >> 3);
+      const int64_t r = min64(m0 + row, M - 1);
+      a_dl[i] = (uint32_t)(r * p.lda * E + (((lane & 7) ^ swz(row)) << 4));
     }
     if constexpr (NT) {
 #pragma unroll
       for (int i = 0; i < BL; ++i) {
-        const char *q = b_src[i] + kofs;
-        if (VEC && full) {
-          rb[i] = load16(q);
-        } else {
-          const int64_t k0 = kt * BK + c * V;
-          const int nv = (int)max64(0, min64(V, K - k0));
-          rb[i] = (VEC && nv == V) ? load16(q) : load_chunk_elems<E>(q, nv);
-        }
+        const int row = wave * (BN / NW) + i * 8 + (lane >> 3);
+        const int64_t r = min64(n0 + row, N - 1);
+        b_dl[i] = (uint32_t)(r * p.ldb * E + (((lane & 7) ^ swz(row)) << 4));
+      }
+    }
+  }
+
+  i32x4 ra[AL], rb[BL];
+
+  // Issue the direct loads of whole K-step kt into `stage` (A, and B when NT).
+  auto issue_direct = [&](int64_t kt, int stage) __attribute__((always_inline)) {
+    const int64_t kofs = kt * kRowBytes;
+    char *la = lds + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < AL; ++i)
+      load16_to_lds(A + kofs + a_dl[i], la + (wave * (BM / NW) + i * 8) * kRowBytes);
+    if constexpr (NT) {
+#pragma unroll
+      for (int i = 0; i < BL; ++i)
+        load16_to_lds(B + kofs + b_dl[i], la + A_BYTES + (wave * (BN / NW) + i * 8) * kRowBytes);
+    }
+  };
+
+  // NN B rows of whole K-step kt into registers.  With N*E a multiple of
+  // 16 a chunk lies wholly inside or wholly outside N; outside ones read
+  // column 0 (nn_src), which only feeds outputs that are never stored.
+  auto load_nn_full = [&](int64_t kt) __attribute__((always_inline)) {
+    const char *bk = B + kt * BK * p.ldb * E;
+#pragma unroll
+    for (int r = 0; r < RNN; ++r) rb[r] = load16(bk + (nn_src + r * ldb_bytes));
+  };
+
+  // Register path for any K-step: element loads, zero past K (and past N for NN).
+  auto load_regs = [&](int64_t kt) __attribute__((always_inline)) {
+    const int64_t kofs = kt * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+      const int64_t k0 = kt * BK + c * V;
+      const int nv = (int)max64(0, min64(V, K - k0));
+      const char *q = A + kofs + a_src[i];
+      ra[i] = (VEC && nv == V) ? load16(q) : load_chunk_elems<E>(q, nv);
+    }
+    if constexpr (NT) {
+#pragma unroll
+      for (int i = 0; i < BL; ++i) {
+        const int64_t k0 = kt * BK + c * V;
+        const int nv = (int)max64(0, min64(V, K - k0));
+        const char *q = B + kofs + b_src[i];
+        rb[i] = (VEC && nv == V) ? load16(q) : load_chunk_elems<E>(q, nv);
       }
     } else {
-      const int64_t rofs = kt * BK * p.ldb * E;  // K-step kt starts BK rows down
+      const char *bk = B + kt * BK * p.ldb * E;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const char *q = b_src[r] + rofs;
-        const bool krow_ok = full || (kt * BK + nn_kb * 8 + r < K);
-        if (VEC && nb_valid == V && krow_ok)
-          rb[r] = load16(q);
-        else
-          rb[r] = load_chunk_elems<E>(q, krow_ok ? nb_valid : 0);
+      for (int r = 0; r < RNN; ++r) {
+        const char *q = bk + (nn_src + r * ldb_bytes);
+        const bool krow_ok = kt * BK + nn_kb * RNN + r < K;
+        rb[r] = (VEC && nb_valid == V && krow_ok) ? load16(q)
+                                                   : load_chunk_elems<E>(q, krow_ok ? nb_valid : 0);
       }
     }
   };
 
-  // Registers -> LDS stage.
-  auto store_step = [&](int stage) {
+  auto store_nn = [&](int stage) __attribute__((always_inline)) {
+    if constexpr (!NT) {
+      store_nn_block<E, RNN>(lds + stage * STAGE + A_BYTES, rb, nn_nc * V, nn_kb * RNN * E);
+    }
+  };
+
+  auto store_regs = [&](int stage) __attribute__((always_inline)) {
     char *la = lds + stage * STAGE;
-    char *lb = la + A_BYTES;
 #pragma unroll
-    for (int i = 0; i < AL; ++i) *(i32x4 *)(la + lds_off((tid >> 3) + 32 * i, c)) = ra[i];
+    for (int i = 0; i < AL; ++i) *(i32x4 *)(la + lds_off((tid >> 3) + (NTH / 8) * i, c)) = ra[i];
     if constexpr (NT) {
 #pragma unroll
-      for (int i = 0; i < BL; ++i) *(i32x4 *)(lb + lds_off((tid >> 3) + 32 * i, c)) = rb[i];
+      for (int i = 0; i < BL; ++i)
+        *(i32x4 *)(la + A_BYTES + lds_off((tid >> 3) + (NTH / 8) * i, c)) = rb[i];
     } else {
-      if (tid < BN) store_nn_block<E>(lb, rb, nn_nc * V, nn_kb * 8 * E);
+      store_nn(stage);
     }
   };
 
   // Fragment addresses: a lane reads row (block base + l32), chunk 2s + g.
-  // Block bases are multiples of 32, so swz(row) = swz(l32).
+  // Block bases are multiples of 32 and each wave's first block a multiple
+  // of 64, so swz(base + l32) = swz(l32) ^ (4 if the block index is odd).
+  static_assert(WTM % 64 == 0 && WTN % 64 == 0, "wave tiles start on 64-row boundaries");
   int choff[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) choff[s] = ((2 * s + g) ^ swz(l32)) << 4;
+  const int a_frag = (wm * WTM + l32) * kRowBytes;
+  const int b_frag = A_BYTES + (wn * WTN + l32) * kRowBytes;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -379,33 +457,104 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute_step = [&](int stage) {
-    const char *la = lds + stage * STAGE;
-    const char *lb = la + A_BYTES;
-    i32x4 fa[4][FM], fb[4][FN];
+  i32x4 fa[4][FM], fb[4][FN];
+  auto read_slot = [&](int stage, int s) __attribute__((always_inline)) {
+    const char *base = lds + stage * STAGE;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int i = 0; i < FM; ++i)
+      fa[s][i] = *(const i32x4 *)(base + a_frag + i * 32 * kRowBytes + (choff[s] ^ ((i & 1) << 6)));
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        fa[s][i] = *(const i32x4 *)(la + (wm * WTM + i * 32 + l32) * kRowBytes + choff[s]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        fb[s][j] = *(const i32x4 *)(lb + (wn * WTN + j * 32 + l32) * kRowBytes + choff[s]);
-    }
-    mma_step<AB, FM, FN>(acc, fa, fb);
+    for (int j = 0; j < FN; ++j)
+      fb[s][j] = *(const i32x4 *)(base + b_frag + j * 32 * kRowBytes + (choff[s] ^ ((j & 1) << 6)));
+  };
+  // Units of phase q (q < 3) of a K-step.
+  auto mma_units_phase = [&](int q) __attribute__((always_inline)) {
+    if (q == 0) mma_units<AB, FM, FN, 0, U / 4>(acc, fa, fb);
+    else if (q == 1) mma_units<AB, FM, FN, U / 4, U / 2>(acc, fa, fb);
+    else mma_units<AB, FM, FN, U / 2, 3 * U / 4>(acc, fa, fb);
+  };
+
+  // All LDS writes of this wave (direct and ds_write) done, then the barrier.
+  auto stage_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
 
   const int64_t nsteps = (K + BK - 1) / BK;
   const int64_t nfull = K / BK;
-  load_step(0, nfull > 0);
-  store_step(0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nsteps; ++kt) {
-    const bool more = kt + 1 < nsteps;
-    if (more) load_step(kt + 1, kt + 1 < nfull);
-    compute_step((int)(kt & 1));
-    if (more) store_step((int)((kt + 1) & 1));
-    __syncthreads();
+
+  // One K-step on stage `cur`, in four phases of U/4 matrix instructions.
+  // The fragments of the first PRE k-slots are already in registers; phase
+  // q reads slot PRE + q, so every slot is read at least one phase before
+  // the instructions that use it.  The next stage is written
+  // in the last phase, well after its global loads were issued; the barrier
+  // falls before the last UL instructions, so the first fragment reads of
+  // stage `nxt` overlap the step's final instructions.  Scheduling barriers
+  // keep the phases apart; group barriers interleave reads and MFMAs.
+  auto step_body = [&](int cur, int nxt, bool from_regs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      if (PRE + q < 4) read_slot(cur, PRE + q);
+      mma_units_phase(q);
+      if (PRE + q < 4) interleave_reads<U / 4, FM + FN>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (from_regs)
+      store_regs(nxt);
+    else
+      store_nn(nxt);
+    mma_units<AB, FM, FN, 3 * U / 4, U - UL>(acc, fa, fb);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_barrier();
+#pragma unroll
+    for (int s0 = 0; s0 < PRE; ++s0) read_slot(nxt, s0);
+    mma_units<AB, FM, FN, U - UL, U>(acc, fa, fb);
+    interleave_reads<UL, PRE * (FM + FN)>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue: step 0 into stage 0
+  if (VEC && nfull > 0) {
+    issue_direct(0, 0);
+    if constexpr (!NT) {
+      load_nn_full(0);
+      store_nn(0);
+    }
+  } else {
+    load_regs(0);
+    store_regs(0);
+  }
+  stage_barrier();
+#pragma unroll
+  for (int s0 = 0; s0 < PRE; ++s0) read_slot(0, s0);
+
+  int64_t kt = 0;
+  if constexpr (VEC) {
+    // steady state: the next step is a whole one
+    for (; kt + 1 < nfull; ++kt) {
+      const int cur = (int)(kt & 1), nxt = cur ^ 1;
+      issue_direct(kt + 1, nxt);
+      if constexpr (!NT) load_nn_full(kt + 1);
+      // keep the global loads here, a whole K-step ahead of their use
+      __builtin_amdgcn_sched_barrier(0);
+      step_body(cur, nxt, false);
+    }
+  }
+  // remaining steps through registers (partial K-step, or the element path)
+  for (; kt + 1 < nsteps; ++kt) {
+    const int cur = (int)(kt & 1), nxt = cur ^ 1;
+    load_regs(kt + 1);
+    step_body(cur, nxt, true);
+  }
+  // last step
+  {
+    const int cur = (int)(kt & 1);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      if (PRE + q < 4) read_slot(cur, PRE + q);
+      mma_units_phase(q);
+    }
+    mma_units<AB, FM, FN, 3 * U / 4, U>(acc, fa, fb);
   }
 
   // ---- epilogue: scale, bias, round once, masked store
@@ -431,11 +580,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmParams p) {
   }
 }
 
-template <int AB, int CT, bool NT, int BM, int BN, bool VEC>
+template <int AB, int CT, bool NT, int BM, int BN, int NW, bool VEC>
 hipError_t launch_one(const GemmParams &p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
-  hipLaunchKernelGGL((gemm_mfma_kernel<AB, CT, NT, BM, BN, VEC>), dim3((unsigned)tiles),
-                     dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((gemm_mfma_kernel<AB, CT, NT, BM, BN, NW, VEC>), dim3((unsigned)tiles),
+                     dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -443,12 +592,13 @@ template <int AB, int CT, bool NT>
 hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t stream) {
   if (vec) {
     switch (tile) {
-      case kTile256x256: return launch_one<AB, CT, NT, 256, 256, true>(p, stream);
-      case kTile256x128: return launch_one<AB, CT, NT, 256, 128, true>(p, stream);
-      default: return launch_one<AB, CT, NT, 128, 128, true>(p, stream);
+      case kTile256x256: return launch_one<AB, CT, NT, 256, 256, 8, true>(p, stream);
+      case kTile256x256w4: return launch_one<AB, CT, NT, 256, 256, 4, true>(p, stream);
+      case kTile256x128: return launch_one<AB, CT, NT, 256, 128, 4, true>(p, stream);
+      default: return launch_one<AB, CT, NT, 128, 128, 4, true>(p, stream);
     }
   }
-  return launch_one<AB, CT, NT, 128, 128, false>(p, stream);
+  return launch_one<AB, CT, NT, 128, 128, 4, false>(p, stream);
 }
 
 template <int AB, int CT>

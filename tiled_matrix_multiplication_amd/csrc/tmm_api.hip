@@ -10,7 +10,7 @@
 
 #include <mutex>
 
-#include "../../include/tmm.h"
+#include "tmm.h"
 #include "tmm_internal.h"
 
 namespace {
@@ -64,6 +64,10 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, cons
   // The grid has one workgroup per 128x128 tile or larger per problem.
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   if (tiles > (int64_t)0x7fffffff / batch) return TMM_ERR_DIM;
+  // Kernels address A and B of one problem with 32-bit byte offsets.
+  if (K > 0 && (((M - 1) * lda + K) * e >= ((int64_t)1 << 32) ||
+                ((trans_b ? (N - 1) * ldb + K : (K - 1) * ldb + N) * e) >= ((int64_t)1 << 32)))
+    return TMM_ERR_DIM;
   return TMM_OK;
 }
 
@@ -84,7 +88,7 @@ int cu_count() {
   return cached[dev];
 }
 
-// TMM_FORCE_TILE = "256x256" | "256x128" | "128x128" pins the tile shape
+// TMM_FORCE_TILE = "256x256" | "256x128" | "128x128" | "256x256w4" pins the tile shape
 // (for measurements); anything else leaves the choice to pick_tile.
 int forced_tile() {
   static int forced = -2;
@@ -95,6 +99,7 @@ int forced_tile() {
       if (!strcmp(s, "256x256")) forced = tmm::kTile256x256;
       else if (!strcmp(s, "256x128")) forced = tmm::kTile256x128;
       else if (!strcmp(s, "128x128")) forced = tmm::kTile128x128;
+      else if (!strcmp(s, "256x256w4")) forced = tmm::kTile256x256w4;
     }
   }
   return forced;
@@ -108,10 +113,10 @@ tmm::Tile pick_tile(int64_t M, int64_t N, int64_t batch, int ab) {
   if (f >= 0) return (tmm::Tile)f;
   if (ab == TMM_F32) return tmm::kTile128x128;
   const int cus = cu_count();
-  const double eff[tmm::kNumTiles] = {1.0, 0.85, 0.65};
+  const double eff[tmm::kNumAutoTiles] = {1.0, 0.85, 0.65};
   tmm::Tile best = tmm::kTile128x128;
   double best_cost = 1e300;
-  for (int t = 0; t < tmm::kNumTiles; ++t) {
+  for (int t = 0; t < tmm::kNumAutoTiles; ++t) {
     const int bm = tmm::tile_bm((tmm::Tile)t), bn = tmm::tile_bn((tmm::Tile)t);
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * batch;
     const int64_t rounds = (tiles + cus - 1) / cus;
@@ -164,10 +169,14 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
     err = tmm::launch_gemv((Fmt)ab, (Fmt)c, vec, g, stream);
   } else {
     const int e = elem_bytes(ab);
-    // 16-byte loads need every row of A and B to start on a 16-byte boundary,
-    // and the batch strides to keep it so.
+    // 16-byte loads need every row of A and B to start on a 16-byte boundary
+    // (and the batch strides to keep it so); NN also needs N*e to be a
+    // multiple of 16 so a 16-byte chunk of a B row is wholly inside or
+    // outside N.
     const bool vec = aligned(A, 16) && aligned(B, 16) && (lda * e) % 16 == 0 &&
-                     (ldb * e) % 16 == 0 && (batch == 1 || ((sA * e) % 16 == 0 && (sB * e) % 16 == 0));
+                     (ldb * e) % 16 == 0 &&
+                     (batch == 1 || ((sA * e) % 16 == 0 && (sB * e) % 16 == 0)) &&
+                     (trans_b || (N * e) % 16 == 0);
     const tmm::Tile tile = vec ? pick_tile(M, N, batch, ab) : tmm::kTile128x128;
     err = dispatch_gemm(ab, c, trans_b != 0, tile, vec, p, stream);
   }

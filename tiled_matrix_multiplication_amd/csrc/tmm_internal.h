@@ -10,8 +10,16 @@ namespace tmm {
 // Element formats, same numbering as tmm_dtype in include/tmm.h.
 enum Fmt : int { kF32 = 0, kBF16 = 1, kF16 = 2, kF8 = 3 };
 
-// Workgroup tile shapes of the MFMA GEMM kernel.
-enum Tile : int { kTile256x256 = 0, kTile256x128 = 1, kTile128x128 = 2, kNumTiles = 3 };
+// Workgroup tile shapes of the MFMA GEMM kernel (the first kNumAutoTiles
+// are chosen by shape; 256x256 runs 8 waves, the others 4; the 4-wave
+// 256x256 variant is only selected by name).
+enum Tile : int {
+  kTile256x256 = 0,
+  kTile256x128 = 1,
+  kTile128x128 = 2,
+  kTile256x256w4 = 3,
+  kNumAutoTiles = 3
+};
 
 struct GemmParams {
   int64_t M, N, K;
@@ -28,7 +36,7 @@ struct GemmParams {
 
 // Rows/columns of a workgroup tile.
 inline int tile_bm(Tile t) { return t == kTile128x128 ? 128 : 256; }
-inline int tile_bn(Tile t) { return t == kTile256x256 ? 256 : 128; }
+inline int tile_bn(Tile t) { return (t == kTile256x256 || t == kTile256x256w4) ? 256 : 128; }
 
 // Launch the tiled MFMA GEMM for one input type with the given tile shape.
 // `vec` selects the 16-byte-load path (every operand row 16-byte aligned);
