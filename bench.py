@@ -22,6 +22,9 @@ supported (one GPU per process, nothing is sharded here).
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -58,6 +61,11 @@ def intensity(M, N, K, in_bytes, out_bytes=None):
     """FLOP per compulsory byte (the arithmetic intensity of the roofline model)."""
     out_bytes = in_bytes if out_bytes is None else out_bytes
     return gemm_flops(M, N, K) / gemm_bytes(M, N, K, in_bytes, out_bytes)
+
+
+def tile_count(M, N, bm, bn):
+    """Output tiles of an M x N result cut into bm x bn tiles (partial edge tiles count)."""
+    return -(-M // bm) * -(-N // bn)
 
 
 def roofline_time(flops, nbytes, peak_tflops, peak_gbs=PEAK_HBM_GBS):
@@ -203,13 +211,88 @@ def roofline_entry(name, r):
     t = r["ms"] * 1e-3
     ai = r["flops"] / r["bytes"]
     ridge = PEAK_TFLOPS[fin] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    traffic = traffic_from_profile(name)
     if ai >= ridge:
         ach = r["flops"] / t / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_TFLOPS[fin], "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_TFLOPS[fin], 4), "traffic": None}
+                "frac": round(ach / PEAK_TFLOPS[fin], 4), "traffic": traffic}
     ach = r["bytes"] / t / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+
+# ---------------------------------------------------------------- HBM traffic
+
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "tiled_matrix_multiplication_amd", "csrc")
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: counter-derived traffic is only reported for
+    the kernel build it was measured on."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(CSRC, "*.hip"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(name):
+    return os.path.join(PROFILES, f"traffic_{name}.json")
+
+
+def traffic_from_profile(name):
+    """HBM bytes per launch from profiles/traffic_<name>.json, or None when
+    absent or measured on other kernel sources."""
+    path = traffic_path(name)
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    return d["bytes_per_launch"] if d.get("source_hash") == kernel_source_hash() else None
+
+
+def _counter_per_dispatch(csv_path, counter, kernel_substr):
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"{csv_path}: no {counter} rows for kernels matching {kernel_substr!r}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes,
+                  kernel_substr="gemm_mfma_kernel", copy_substr="copy"):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the workload's kernel by
+    what the same counters read for a plain copy of `copy_bytes` bytes."""
+    if name == "gemv":
+        kernel_substr = "gemv"
+    f_k, nf = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", kernel_substr)
+    w_k, nw = _counter_per_dispatch(write_csv, "WRITE_SIZE", kernel_substr)
+    f_c, _ = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", copy_substr)
+    w_c, _ = _counter_per_dispatch(copy_write_csv, "WRITE_SIZE", copy_substr)
+    fetch_scale = copy_bytes / f_c     # bytes per counter unit, from the copy's reads
+    write_scale = copy_bytes / w_c
+    out = {"workload": describe(name), "source_hash": kernel_source_hash(),
+           "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k, "dispatches": [nf, nw],
+           "copy_bytes": copy_bytes, "copy_fetch_kib": f_c, "copy_write_kib": w_c,
+           "fetch_bytes": f_k * fetch_scale, "write_bytes": w_k * write_scale,
+           "bytes_per_launch": f_k * fetch_scale + w_k * write_scale}
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    out["algorithmic_bytes"] = gemm_bytes(M, N, K, BYTES[fin], BYTES[fout], Z, bias)
+    os.makedirs(PROFILES, exist_ok=True)
+    json.dump(out, open(traffic_path(name), "w"), indent=1)
+    print(json.dumps(out))
+
+
+def copy_calibration(nbytes, steps):
+    """A plain device-to-device copy of `nbytes` (torch's copy kernel), for
+    calibrating the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": steps}))
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -223,7 +306,7 @@ def compare_rows(C, idx, o):
     return float(np.linalg.norm(g - o) / den) if den > 0 else float(np.linalg.norm(g - o))
 
 
-def cpu_baseline(name, r, target_s=12.0):
+def cpu_baseline(name, r, target_s=20.0):
     """The oracle, as it stands, on a row sample of the workload's first problem.
 
     Times it on the host cores (OpenMP threads), scales to the metric's unit,
@@ -241,19 +324,27 @@ def cpu_baseline(name, r, target_s=12.0):
         o = oracle.gemm(fin, np.ascontiguousarray(A[idx]), B, trans_b=tb, bias=bvec, scale_a=sa, scale_b=sb)
         return idx, o, time.perf_counter() - t0
 
-    rows = min(M, 8)
-    idx, o, t = run_rows(rows)
-    if t < target_s / 4 and rows < M:
-        rows = int(min(M, max(rows, rows * target_s / max(t, 1e-3))))
-        idx, o, t = run_rows(rows)
+    # two small runs separate the fixed cost (decoding B) from the per-row cost
+    idx, o, t8 = run_rows(min(M, 8))
+    if M > 8:
+        idx, o, t64 = run_rows(min(M, 64))
+        per_row = max((t64 - t8) / max(min(M, 64) - 8, 1), 1e-6)
+        rows = int(min(M, max(64, (target_s - t8) / per_row)))
+        if rows > len(idx):
+            idx, o, t = run_rows(rows)
+        else:
+            t = t64
+    else:
+        t = t8
     flops = gemm_flops(len(idx), N, K)
     C = r["sets"][0][2]
     C0 = C[0] if Z > 1 else C
     err = compare_rows(C0, idx, o)
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
             "kind": "oracle", "seconds": round(t, 2),
-            "sample": f"{len(idx)} of {M} rows of the {describe(name)} product "
-                      f"({len(idx)}x{N}x{K}, fp64 triple loop)",
+            "sample": (f"{len(idx)} of {M} rows" if len(idx) < M else f"all {M} rows") +
+                      f" of the {describe(name)} product ({len(idx)}x{N}x{K}, fp64 triple loop; "
+                      f"time includes decoding the inputs)",
             "sample_rel_fro_vs_gpu": err}
 
 
@@ -265,7 +356,17 @@ def main(argv=None):
     ap.add_argument("--workload", default="square_bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-gemv", action="store_true", help="skip the GEMV side measurement")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES, --steps times (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                         "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE outputs of --workload and of "
+                         "--copy-calib into profiles/traffic_<workload>.json")
+    ap.add_argument("--copy-bytes", type=int, default=0, help="bytes of the calibration copy")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        summarize_pmc(args.workload, *args.summarize_pmc, copy_bytes=args.copy_bytes)
+        return 0
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this library runs on one GPU per "
               "process and shards nothing (run with --gpus 1)", file=sys.stderr)
@@ -275,6 +376,9 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_calib:
+        copy_calibration(args.copy_calib, args.steps)
+        return 0
     import tiled_matrix_multiplication_amd  # noqa: F401  (fails loudly without libtmm.so)
     dev = "cuda:0"
     name = args.workload
@@ -307,7 +411,7 @@ def main(argv=None):
         line["gemv"] = {"workload": describe("gemv"), "us_per_launch": round(g["ms"] * 1e3, 3),
                         "bytes_per_launch": int(g["bytes"]), "achieved": round(gbs, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                        "weight_copies_rotated": g["copies"]}
+                        "weight_copies_rotated": g["copies"], "traffic": traffic_from_profile("gemv")}
         del g
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(name, r)

@@ -249,17 +249,19 @@ __device__ __forceinline__ void store_nn_block(char *lds_b, const i32x4 (&in)[R]
   }
 }
 
-// Scheduling hint: NR (LDS read, MFMA) pairs, then the remaining MFMAs of
-// the region, so the reads issue between matrix instructions.
-template <int NM, int NR>
-__device__ __forceinline__ void interleave_reads() {
-#pragma unroll
-  for (int i = 0; i < NR && i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-  }
-  if constexpr (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
-  if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+// Scheduling hint for a region holding NM MFMAs, NR LDS reads and NV
+// global loads: two MFMAs, then the loads and LDS reads, then the other
+// MFMAs.  The compiler puts a full LDS wait (lgkmcnt(0)) before a region's
+// first MFMA when loop-carried fragments and direct-to-LDS loads are in
+// flight; issuing the region's own reads after that MFMA keeps the wait
+// from covering them, and they still get most of the region to complete.
+template <int NM, int NR, int NV = 0>
+__device__ __forceinline__ void interleave() {
+  constexpr int lead = NM < 2 ? NM : 2;
+  if constexpr (lead > 0) __builtin_amdgcn_sched_group_barrier(0x008, lead, 0);    // MFMAs
+  if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);        // LDS reads
+  if constexpr (NV > 0) __builtin_amdgcn_sched_group_barrier(0x020, NV, 0);        // global loads
+  if constexpr (NM > lead) __builtin_amdgcn_sched_group_barrier(0x008, NM - lead, 0);
 }
 
 // ---------------------------------------------------------------- kernel
@@ -491,12 +493,29 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
   // falls before the last UL instructions, so the first fragment reads of
   // stage `nxt` overlap the step's final instructions.  Scheduling barriers
   // keep the phases apart; group barriers interleave reads and MFMAs.
-  auto step_body = [&](int cur, int nxt, bool from_regs) __attribute__((always_inline)) {
+  // Whole K-steps (!from_regs) issue the next step's global loads inside
+  // phases 0 (direct A / NT B) and 1 (NN B into registers).
+  constexpr int NV0 = AL + (NT ? BL : 0);
+  constexpr int NV1 = NT ? 0 : RNN;
+  constexpr int NR = FM + FN;
+  auto step_body = [&](int64_t kt, int cur, int nxt, bool from_regs) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       if (PRE + q < 4) read_slot(cur, PRE + q);
+      if (!from_regs && q == 0) issue_direct(kt + 1, nxt);
+      if constexpr (!NT) {
+        if (!from_regs && q == 1) load_nn_full(kt + 1);
+      }
       mma_units_phase(q);
-      if (PRE + q < 4) interleave_reads<U / 4, FM + FN>();
+      if (from_regs) {
+        if (PRE + q < 4) interleave<U / 4, NR>();
+      } else if (q == 0) {
+        interleave<U / 4, (PRE < 4 ? NR : 0), NV0>();
+      } else if (q == 1) {
+        interleave<U / 4, (PRE + 1 < 4 ? NR : 0), NV1>();
+      } else {
+        if (PRE + q < 4) interleave<U / 4, NR>();
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (from_regs)
@@ -509,7 +528,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
     for (int s0 = 0; s0 < PRE; ++s0) read_slot(nxt, s0);
     mma_units<AB, FM, FN, U - UL, U>(acc, fa, fb);
-    interleave_reads<UL, PRE * (FM + FN)>();
+    interleave<UL, PRE * NR>();
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -533,18 +552,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
     // steady state: the next step is a whole one
     for (; kt + 1 < nfull; ++kt) {
       const int cur = (int)(kt & 1), nxt = cur ^ 1;
-      issue_direct(kt + 1, nxt);
-      if constexpr (!NT) load_nn_full(kt + 1);
-      // keep the global loads here, a whole K-step ahead of their use
-      __builtin_amdgcn_sched_barrier(0);
-      step_body(cur, nxt, false);
+      step_body(kt, cur, nxt, false);
     }
   }
   // remaining steps through registers (partial K-step, or the element path)
   for (; kt + 1 < nsteps; ++kt) {
     const int cur = (int)(kt & 1), nxt = cur ^ 1;
     load_regs(kt + 1);
-    step_body(cur, nxt, true);
+    step_body(kt, cur, nxt, true);
   }
   // last step
   {
