@@ -11,10 +11,12 @@ Tolerances (the pages give none; these follow from the arithmetic):
     |g - o| <= ulp(R(o)) + 4 sqrt(K) 2^-24 T  with T = sum_k |a_ik b_kj|
     (probabilistic fp32 summation bound with lambda = 4);
   * fp8 inputs: relative Frobenius error <= 1e-3 (fp32 output: against o;
-    bf16 output: against R(o), on top of the 1-ulp rule).  The gfx950 fp8
-    matrix instruction aligns the products of one instruction to the largest
-    one and drops low-order bits (448 + 63 * 2^-9 sums to 448.109375, not
-    448.123046875), so fp8 sums are not held to the fp32 1e-5 figure.
+    bf16 output: against R(o), on top of the 1-ulp rule, whose allowance
+    grows by 1e-3 T per element).  The gfx950 fp8 matrix instruction aligns
+    the products of one instruction to the largest one and drops low-order
+    bits (448 + 63 * 2^-9 sums to 448.109375, not 448.123046875), so fp8
+    sums are not held to the fp32 figures: an output that cancels to far
+    below T can be off by many of its own ulps.
 """
 from __future__ import annotations
 
@@ -86,15 +88,16 @@ def check_f32(g: torch.Tensor, o: np.ndarray, tol: float = FRO_TOL_F32, what: st
 
 
 def check_rounded(g: torch.Tensor, o: np.ndarray, T: np.ndarray, K: int, what: str = "",
-                  fro_tol: float | None = None):
-    """1-ulp rule for bf16/fp16 outputs, with the cancellation allowance."""
+                  fro_tol: float | None = None, extra_rel: float = 0.0):
+    """1-ulp rule for bf16/fp16 outputs, with the cancellation allowance
+    (widened by extra_rel * T for arithmetic coarser than fp32)."""
     f = fmt_of(g)
     gb = to_bits(g)
     gv = oracle.decode(f, gb)
     r = oracle.decode(f, oracle.round_to(f, o))
     u = ulp(f, r)
     ok = np.abs(gv - r) <= u
-    bound = LAMBDA * math.sqrt(max(K, 1)) * 2.0 ** -24 * T
+    bound = (LAMBDA * math.sqrt(max(K, 1)) * 2.0 ** -24 + extra_rel) * T
     loose = ~ok & (np.abs(gv - o) <= u + bound)
     bad = ~(ok | loose)
     n = int(bad.sum())
@@ -114,4 +117,5 @@ def check(g: torch.Tensor, o: np.ndarray, T: np.ndarray | None, K: int, exact: b
         return check_exact(g, o, what)
     if fmt_of(g) == "f32":
         return check_f32(g, o, tol=FRO_TOL_F8 if f8 else FRO_TOL_F32, what=what)
-    return check_rounded(g, o, T, K, what=what, fro_tol=FRO_TOL_F8 if f8 else None)
+    return check_rounded(g, o, T, K, what=what, fro_tol=FRO_TOL_F8 if f8 else None,
+                         extra_rel=FRO_TOL_F8 if f8 else 0.0)

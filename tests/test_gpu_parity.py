@@ -7,59 +7,15 @@ import torch
 
 import oracle
 import synthetic as syn
+from gpu_cases import DEV, TORCH_DT, gemm_case, on_gpu
 from parity import check, to_bits
 
 pytestmark = pytest.mark.gpu
-
-DEV = "cuda:0"
-TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
-            "e4m3": torch.float8_e4m3fn}
-
 
 @pytest.fixture(scope="module")
 def tmm():
     import tiled_matrix_multiplication_amd as t
     return t
-
-
-def on_gpu(bits: np.ndarray, fmt: str) -> torch.Tensor:
-    return syn.as_torch(bits, fmt).to(DEV)
-
-
-def make_operand(shape, fmt, dist, seed, pad=0, scale=None):
-    """Bits of a (rows, cols) operand, stored with `pad` extra elements per row.
-    Returns (full padded bits, view of the logical part, fp8 scale)."""
-    rows, cols = shape
-    if dist == "int":
-        x = syn.small_ints((rows, cols + pad), seed)
-    else:
-        x = syn.normal((rows, cols + pad), seed)
-    s = np.float32(1.0)
-    if fmt == "e4m3":
-        if dist != "int":
-            s = syn.e4m3_scale(x[:, :cols])
-        bits = syn.quantize_e4m3(x, s)
-    else:
-        bits = syn.to_bits(x, fmt)
-    return bits, bits[:, :cols], s
-
-
-def gemm_case(tmm, M, N, K, fmt, out, trans_b, dist, bias, seed=0, pad=0):
-    A_full, A, sa = make_operand((M, K), fmt, dist, seed + 1, pad)
-    bshape = (N, K) if trans_b else (K, N)
-    B_full, B, sb = make_operand(bshape, fmt, dist, seed + 2, pad)
-    bvec = None
-    if bias:
-        bvec = (syn.small_ints((N,), seed + 3) if dist == "int" else syn.normal((N,), seed + 3, 0.02))
-        bvec = bvec.astype(np.float32)
-    o, T = oracle.gemm(fmt, A, B, trans_b=trans_b, bias=bvec, scale_a=sa, scale_b=sb, want_abs=True)
-    dA = on_gpu(A_full, fmt)[:, :K]
-    dB = on_gpu(B_full, fmt)[:, :bshape[1]]
-    dC = torch.full((M, N), float("nan"), dtype=TORCH_DT[out], device=DEV)
-    dbias = torch.from_numpy(bvec).to(DEV) if bvec is not None else None
-    tmm.tmm_gemm(dA, dB, dC, bias=dbias, trans_b=trans_b, scale_a=float(sa), scale_b=float(sb))
-    torch.cuda.synchronize()
-    return dC, o, T
 
 
 # (M, N, K, in, out, trans_b, dist, bias, pad)
@@ -276,3 +232,43 @@ def test_gemv_parity(tmm, N, K, fmt, out, dist, bias):
     tmm.tmm_gemm(on_gpu(x, fmt), on_gpu(W, fmt), y2, trans_b=True,
                  bias=torch.from_numpy(b).to(DEV) if b is not None else None)
     assert torch.equal(y2.view(N), y)
+
+
+def test_graph_replay_matches_eager(tmm):
+    """GEMV and GEMM launches captured in a HIP graph (as the GEMV is timed)
+    give the eager result on every replay, with eager work and
+    synchronisations between the replays and new inputs written in place."""
+    N, K = 1024, 768
+    M = 300
+    W = on_gpu(syn.to_bits(syn.normal((N, K), 81, 0.02), "bf16"), "bf16")
+    A = on_gpu(syn.to_bits(syn.normal((M, K), 82), "bf16"), "bf16")
+    x = torch.empty(K, dtype=torch.bfloat16, device=DEV)
+    bias = torch.from_numpy(syn.normal((N,), 83, 0.02)).to(DEV)
+    y = torch.empty(N, dtype=torch.bfloat16, device=DEV)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    x.copy_(on_gpu(syn.to_bits(syn.normal((1, K), 84), "bf16"), "bf16").view(K))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tmm.tmm_gemv(W, x, y, bias=bias)
+        tmm.tmm_gemm(A, W, C, bias=bias, trans_b=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        tmm.tmm_gemv(W, x, y, bias=bias)
+        tmm.tmm_gemm(A, W, C, bias=bias, trans_b=True)
+    for r in range(4):
+        x.copy_(on_gpu(syn.to_bits(syn.normal((1, K), 90 + r), "bf16"), "bf16").view(K))
+        A.mul_(-1.0)
+        y.fill_(float("nan"))
+        C.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        y_ref = torch.empty_like(y)
+        C_ref = torch.empty_like(C)
+        tmm.tmm_gemv(W, x, y_ref, bias=bias)
+        tmm.tmm_gemm(A, W, C_ref, bias=bias, trans_b=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"GEMV replay {r} differs from the eager call"
+        assert torch.equal(C, C_ref), f"GEMM replay {r} differs from the eager call"

@@ -28,7 +28,8 @@
 //   * Epilogue: fp8 dequantisation scale, bias per output column, one
 //     round-to-nearest-even conversion, masked stores (the fused epilogue of
 //     the Lecture 27 fused-convolution listing; bias per output feature from
-//     the linear-layer formula of the GEMM page).
+//     the linear-layer formula of the GEMM page).  A store instruction
+//     writes two rows x 32 columns: whole 128-byte lines for fp32 output.
 //   * Edges: rows past M (columns past N) of A (op(B)) are read from the
 //     last valid row, which only feeds outputs that are never stored; the K
 //     tail is zero-filled; stores are masked (tiled_matmul's min() bounds).
@@ -143,6 +144,93 @@ __device__ __forceinline__ void store_out(char *C, int64_t idx, float v) {
     ((uint16_t *)C)[idx] = f32_to_bf16_rne(v);
   else
     ((uint16_t *)C)[idx] = f32_to_f16_rne(v);
+}
+
+// Output bits of v in the output type (fp32, or bf16 / fp16 nearest-even).
+template <int CT>
+__device__ __forceinline__ uint32_t out_bits(float v) {
+  if constexpr (CT == kF32) return __float_as_uint(v);
+  else if constexpr (CT == kBF16) return f32_to_bf16_rne(v);
+  else return f32_to_f16_rne(v);
+}
+
+// Row pitch (bytes) of a wave's epilogue staging area for WT columns: the
+// row plus 32 bytes, so rows r and r + 4 (one store instruction of the
+// accumulator layout) start 32 banks apart.
+template <int CT, int WT>
+constexpr int stage_pitch() { return WT * FmtBytes<CT>::value + 32; }
+
+// Epilogue through LDS.  For each 32-row band i of the wave's block, the
+// accumulators go to the wave's own LDS area `st` (32 rows, stage_pitch
+// bytes apart) as finished output values (v = scale * acc + bias, rounded
+// once), then come back 16 bytes per lane along the rows, so every global
+// store instruction writes whole row segments (4 rows of 256 bytes for a
+// 64-column fp32 block) instead of 32-column pieces of two rows.  Stores are
+// masked by M and N; a 16-byte piece that crosses N, or any piece when C or
+// its row pitch is not 16-byte aligned, is stored element by element.  The
+// caller has finished every LDS read of the main loop (barrier) before this.
+template <int CT, int FM, int FN>
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[FM][FN], char *st, char *C,
+                                               int64_t ldc, int64_t M, int64_t N, int64_t row0,
+                                               int64_t col0, const float *bias, float scale,
+                                               int lane) {
+  constexpr int CE = FmtBytes<CT>::value;
+  constexpr int WT = FN * 32;                 // columns of the wave's block
+  constexpr int RB = WT * CE;                 // bytes of one row of it
+  constexpr int P = stage_pitch<CT, WT>();
+  constexpr int CPR = RB / 16;                // 16-byte pieces per row
+  constexpr int EPC = 16 / CE;                // elements per piece
+  constexpr int NRD = 32 * CPR / 64;          // read instructions per band
+  static_assert(NRD >= 1 && (32 * CPR) % 64 == 0, "epilogue geometry");
+  const int l32 = lane & 31, g = lane >> 5;
+  const bool vec = ((uintptr_t)C % 16) == 0 && ((ldc * CE) % 16) == 0;
+  float bv[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t col = col0 + j * 32 + l32;
+    bv[j] = (bias && col < N) ? bias[col] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    if (row0 + i * 32 >= M) break;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+        const uint32_t b = out_bits<CT>(acc[i][j][r] * scale + bv[j]);
+        char *d = st + row * P + (j * 32 + l32) * CE;
+        if constexpr (CE == 4) *(uint32_t *)d = b;
+        else *(uint16_t *)d = (uint16_t)b;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < NRD; ++t) {
+      const int c = t * 64 + lane;
+      const int row = c / CPR, pc = c % CPR;
+      const i32x4 v = *(const i32x4 *)(st + row * P + pc * 16);
+      const int64_t grow = row0 + i * 32 + row;
+      const int64_t gcol = col0 + (int64_t)pc * EPC;
+      if (grow >= M || gcol >= N) continue;
+      char *dst = C + (grow * ldc + gcol) * CE;
+      if (vec && gcol + EPC <= N) {
+        *(i32x4 *)dst = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          if (gcol + e < N) {
+            const uint32_t w = (uint32_t)v[(e * CE) / 4];
+            if constexpr (CE == 4) ((uint32_t *)dst)[e] = w;
+            else ((uint16_t *)dst)[e] = (uint16_t)(w >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next band's writes
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
 // Matrix instructions of one K-step (128 bytes of K per row), numbered
@@ -572,27 +660,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
     mma_units<AB, FM, FN, 3 * U / 4, U>(acc, fa, fb);
   }
 
-  // ---- epilogue: scale, bias, round once, masked store
+  // ---- epilogue: scale, bias, round once, masked store, staged through
+  // LDS (free once every wave has passed this barrier)
+  static_assert(NW * 32 * stage_pitch<CT, BN / (NW / 2)>() <= 2 * STAGE, "epilogue staging");
+  __syncthreads();
   char *C = (char *)p.C + z * p.strideC * CE;
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int64_t col = n0 + wn * WTN + j * 32 + l32;
-    if (col >= N) continue;
-    const float bv = p.bias ? p.bias[col] : 0.f;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (row < M) {
-          float v = acc[i][j][r];
-          if constexpr (AB == kF8) v *= p.scale;
-          v += bv;
-          store_out<CT>(C, row * p.ldc + col, v);
-        }
-      }
-    }
-  }
+  store_tile_lds<CT, FM, FN>(acc, lds + wave * 32 * stage_pitch<CT, WTN>(), C, p.ldc, M, N,
+                             m0 + wm * WTM, n0 + wn * WTN, p.bias, AB == kF8 ? p.scale : 1.f,
+                             lane);
 }
 
 template <int AB, int CT, bool NT, int BM, int BN, int NW, bool VEC>
@@ -603,11 +678,24 @@ hipError_t launch_one(const GemmParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int AB, int CT, bool NT, int NW>
+hipError_t launch_ring(const GemmParams &p, hipStream_t stream);
+
 template <int AB, int CT, bool NT>
 hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t stream) {
   if (vec) {
     switch (tile) {
-      case kTile256x256: return launch_one<AB, CT, NT, 256, 256, 8, true>(p, stream);
+      case kTile256x256:
+      case kTile256x256r:
+        // Four-stage ring kernel (gemm_ring.h) for 16-bit inputs and whole
+        // K-steps; chosen automatically for an N-contiguous B, where it
+        // measured faster (with a K-contiguous B the two-stage kernel was).
+        if constexpr (AB == kBF16 || AB == kF16) {
+          if (p.K % 32 == 0 && (!NT || tile == kTile256x256r))
+            return launch_ring<AB, CT, NT, 8>(p, stream);
+        }
+        return launch_one<AB, CT, NT, 256, 256, 8, true>(p, stream);
+      case kTile256x256s2: return launch_one<AB, CT, NT, 256, 256, 8, true>(p, stream);
       case kTile256x256w4: return launch_one<AB, CT, NT, 256, 256, 4, true>(p, stream);
       case kTile256x128: return launch_one<AB, CT, NT, 256, 128, 4, true>(p, stream);
       default: return launch_one<AB, CT, NT, 128, 128, 4, true>(p, stream);

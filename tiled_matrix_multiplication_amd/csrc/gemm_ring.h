@@ -1,0 +1,299 @@
+// Tiled GEMM on gfx950 matrix cores with a four-stage LDS ring: the main
+// kernel for 256x256 output tiles when every operand row is 16-byte aligned
+// and K is a multiple of the K-step.
+//
+//   C[z] = scale * A[z] . op(B[z]) (+ bias),  row-major, z < batch
+//
+// Against the two-stage kernel in gemm_mfma.h (which serves every other
+// case), this one keeps global loads three K-steps ahead of their use:
+//   * a K-step is 64 bytes of K per tile row (32 bf16/fp16); a stage
+//     holds A (256 rows x 64 B) and B (16 KiB), 32 KiB, and four stages fill
+//     128 KiB of the 160 KiB LDS;
+//   * both operands move global->LDS with 16-byte direct loads (no
+//     registers): at step k each wave issues its share of step k+3 into the
+//     stage step k-1 used, and before the step's barrier it waits only for
+//     the loads of step k+2 (those of step k+3 stay in flight), so that the
+//     fragments of step k+1 are read during step k -- the
+//     pipelining the MLC GPU-programming tutorial (devtrends.cc review)
+//     describes for TMA, and the double buffering of the Lecture 27 notes
+//     section 2.5 taken one level deeper;
+//   * A and a K-contiguous B (trans_b) keep 64-byte rows, chunk c of row r
+//     at position c ^ ((r >> 2) & 3): 16 consecutive rows read at one chunk
+//     fall on 16 distinct bank groups;
+//   * an N-contiguous B (NN, 16-bit types) is stored as it is in memory,
+//     k-rows of BN elements, 16-byte chunk c of row r at c ^ 4 (r & 3), and
+//     the MFMA's B fragments (8 consecutive k of one column per lane) are
+//     read with the gfx950 transposing LDS read ds_read_b64_tr_b16: in a
+//     group of 16 lanes, output lane i, element e is element (i mod 4) of the
+//     8 bytes addressed by lane 4e + i/4, so pointing lane s at k-row
+//     k0 + s/4, columns n0 + 4 (s mod 4) hands lane i the values
+//     B[k0 .. k0+3][n0 + i];
+//   * NW = 8 waves (two per SIMD) each own a 128x64 block of C as 4x2
+//     32x32 accumulators.  NW = 4 (one wave per SIMD, 128x128 blocks as
+//     4x4: a third fewer LDS fragment reads per matrix instruction) also
+//     compiles but measured slower and is not dispatched.  Tile order and
+//     edges as in gemm_mfma.h; the epilogue is store_tile_lds.
+#pragma once
+
+#include "gemm_mfma.h"
+
+namespace tmm {
+namespace gemm_detail {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kRingStages = 4;
+constexpr int kRingRowBytes = 64;  // bytes of K per tile row per step
+
+__device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
+
+// 16-byte direct global->LDS load: lane L's 16 bytes land at LDS byte
+// address m0 + 16 L.  Written as assembly so that the compiler does not
+// track it: its own tracking of such loads makes every later transposing
+// LDS read wait for all of them (vmcnt(0)), which would drain the ring.
+// The kernel orders these loads itself (s_waitcnt before each barrier, and
+// none left in flight at exit).  One wait state separates the M0 write from
+// its use by an LDS DMA on gfx9.
+__device__ __forceinline__ void dma16(const char *g, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(m0) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// Transposing 8-byte LDS read (see the header comment).  Kept out of lambdas
+// for the same host-pass reason as load16_to_lds.
+__device__ __forceinline__ s16x4 lds_read_tr16(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(__attribute__((address_space(3))) char *)p);
+}
+
+template <int AB, int CT, bool NT, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int E = FmtBytes<AB>::value;
+  constexpr int CE = FmtBytes<CT>::value;
+  constexpr int BK = kRingRowBytes / E;            // K per step
+  constexpr int WGN = NW / 2, WTM = BM / 2, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;      // 4 x 2 accumulators per wave
+  constexpr int A_BYTES = BM * kRingRowBytes;      // 16 KiB
+  constexpr int B_BYTES = BN * kRingRowBytes;      // 16 KiB (NT: BN rows x 64 B; NN: BK rows x BN*E B)
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int NB_ROW = BN * E;                   // NN: bytes of one k-row of the B stage
+  constexpr int LA = A_BYTES / 1024 / NW;          // direct loads per wave per step (A)
+  constexpr int LB = B_BYTES / 1024 / NW;          // (B)
+  constexpr int LPS = LA + LB;
+  static_assert(E == 2, "ring path: 16-bit inputs (fp8 and fp32 use the two-stage kernel)");
+  static_assert((NW == 8 || NW == 4) && LA == 16 / NW && LB == 16 / NW, "ring geometry");
+
+  __shared__ __attribute__((aligned(16))) char lds[kRingStages * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int g = lane >> 5, l32 = lane & 31;
+
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  int64_t pid = remap_xcd(blockIdx.x, (int64_t)gridDim.x);
+  const int64_t z = pid / tiles;
+  pid -= z * tiles;
+  int64_t tm, tn;
+  group_order(pid, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  const char *A = (const char *)p.A + z * p.strideA * E;
+  const char *B = (const char *)p.B + z * p.strideB * E;
+
+  // ---- direct-load sources: byte offsets (< 4 GiB, checked by the host).
+  // A (and NT B): instruction i of wave w fills stage rows w*32 + 16 i ..+15;
+  // lane L lands at row L/4, position L%4 and loads logical chunk
+  // (L%4) ^ swz64(row).
+  uint32_t a_off[LA], b_off[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int row = wave * (BM / NW) + i * 16 + (lane >> 2);
+    const int64_t r = min64(m0 + row, M - 1);
+    a_off[i] = (uint32_t)(r * p.lda * E + (((lane & 3) ^ swz64(row)) << 4));
+  }
+  if constexpr (NT) {
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int row = wave * (BN / NW) + i * 16 + (lane >> 2);
+      const int64_t r = min64(n0 + row, N - 1);
+      b_off[i] = (uint32_t)(r * p.ldb * E + (((lane & 3) ^ swz64(row)) << 4));
+    }
+  } else {
+    // NN: instruction i of wave w fills k-rows w*4 + 2 i, +1 of the stage
+    // (NB_ROW = 512 bytes each); lane L lands at row L/32, position L%32 and
+    // loads logical chunk (L%32) ^ 4 (row & 3).  A chunk wholly past N (the
+    // host ensures N*E % 16 == 0) reads chunk 0 instead; it only feeds
+    // outputs that are never stored.
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int row = wave * (BK / NW) + i * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (row & 3));
+      const int64_t col = n0 + (int64_t)c * (16 / E);
+      const int64_t ccol = col < N ? col : n0;
+      b_off[i] = (uint32_t)(((int64_t)row * p.ldb + ccol) * E);
+    }
+  }
+  const int64_t kstep_b = NT ? (int64_t)kRingRowBytes : (int64_t)BK * p.ldb * E;
+
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int64_t kt, int stage) __attribute__((always_inline)) {
+    const uint32_t la = lds0 + (uint32_t)(stage * STAGE);
+    const char *ak = A + kt * kRingRowBytes;
+    const char *bk = B + kt * kstep_b;
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      dma16(ak + a_off[i], la + (wave * (BM / NW) + i * 16) * kRingRowBytes);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      if constexpr (NT)
+        dma16(bk + b_off[i], la + A_BYTES + (wave * (BN / NW) + i * 16) * kRingRowBytes);
+      else
+        dma16(bk + b_off[i], la + A_BYTES + (wave * (BK / NW) + i * 2) * NB_ROW);
+    }
+  };
+
+  // ---- fragment reads.  k-slot s (0, 1) of a step: lane group g reads chunk
+  // 2s + g of its A row (8 elements of K).
+  // Block bases are multiples of 32 rows, so swz64(base + l32) = swz64(l32).
+  const int a_frag = (wm * WTM + l32) * kRingRowBytes;
+  int a_ch[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) a_ch[s] = ((2 * s + g) ^ swz64(l32)) << 4;
+  // NN transposing reads: lane (G = lane/16, q = lane%16) of a 32-column block
+  // starting at column jb reads k-row 16 s + 8 (G/2) + 4 h + q/4, columns
+  // jb + 16 (G%2) + 4 (q%4) .. +3 (h = 0, 1 gives 8 consecutive k).
+  const int G = lane >> 4, q = lane & 15;
+  const int tr_row0 = 8 * (G >> 1) + (q >> 2);       // + 16 s + 4 h
+  const int tr_col0 = wn * WTN + 16 * (G & 1) + 4 * (q & 3);  // + 32 j (elements)
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Issue order b0, a0, b1, a1, a2, a3: the first matrix instructions of a
+  // slot (blocks (0,0), (0,1), (1,0), ...) wait for as few reads as possible.
+  i32x4 fa[2][FM], fb[2][FN];
+  auto read_a = [&](const char *base, int s, int i) __attribute__((always_inline)) {
+    fa[s][i] = *(const i32x4 *)(base + a_frag + i * 32 * kRingRowBytes + a_ch[s]);
+  };
+  auto read_slot = [&](int stage, int s) __attribute__((always_inline)) {
+    const char *base = lds + stage * STAGE;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (NT) {
+        fb[s][j] = *(const i32x4 *)(base + A_BYTES + (wn * WTN + j * 32 + l32) * kRingRowBytes + a_ch[s]);
+      } else {
+        s16x4 h2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 16 * s + 4 * h + tr_row0;
+          const int col = tr_col0 + 32 * j;                 // element index in the k-row
+          const int chunk = (col * E) >> 4, within = (col * E) & 15;
+          h2[h] = lds_read_tr16(base + A_BYTES + row * NB_ROW + ((chunk ^ (4 * (row & 3))) << 4) + within);
+        }
+        fb[s][j] = i32x4{(int)((uint16_t)h2[0][0] | ((uint32_t)(uint16_t)h2[0][1] << 16)),
+                         (int)((uint16_t)h2[0][2] | ((uint32_t)(uint16_t)h2[0][3] << 16)),
+                         (int)((uint16_t)h2[1][0] | ((uint32_t)(uint16_t)h2[1][1] << 16)),
+                         (int)((uint16_t)h2[1][2] | ((uint32_t)(uint16_t)h2[1][3] << 16))};
+      }
+      read_a(base, s, j);
+    }
+#pragma unroll
+    for (int i = FN; i < FM; ++i) read_a(base, s, i);
+  };
+
+  // MFMAs of k-slot s, instructions [u0, u1) of the slot's FM*FN.
+  auto mma = [&](int s, int u0, int u1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = u0; u < u1; ++u) {
+      const int i = u / FN, j = u % FN;
+      if constexpr (AB == kBF16) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[s][i]),
+                                                            __builtin_bit_cast(bf16x8, fb[s][j]),
+                                                            acc[i][j], 0, 0, 0);
+      } else {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[s][i]),
+                                                           __builtin_bit_cast(f16x8, fb[s][j]),
+                                                           acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  constexpr int NU = FM * FN;       // MFMAs per k-slot
+  constexpr int NR = FM + FN * (NT ? 1 : 2);  // LDS read instructions per slot
+  // s_waitcnt immediates (gfx9: vmcnt bits 3:0, expcnt 6:4 left at 7,
+  // lgkmcnt 11:8 = 0): at most one step's loads left in flight, or none.
+  constexpr int kWait1 = LPS | (7 << 4);
+  constexpr int kWait0 = 7 << 4;
+  static_assert(LPS < 16, "vmcnt field");
+
+  // Wait for step `next`'s loads when the newest issued step is `newest`
+  // (never more than one step later).
+  auto wait_for = [&](int64_t next, int64_t newest) __attribute__((always_inline)) {
+    if (newest > next) __builtin_amdgcn_s_waitcnt(kWait1);
+    else __builtin_amdgcn_s_waitcnt(kWait0);
+  };
+
+  const int64_t nsteps = K / BK;  // the host guarantees K % BK == 0, K > 0
+  // Barrier b(k), at the end of step k, publishes step k+2: the fragments of
+  // step k+1 can then be read during step k, under its matrix instructions,
+  // and no LDS read waits behind a barrier.  Stage (k+3) mod 4, which step k
+  // loads, was last read during step k-1, before b(k-1).
+  const int64_t pro = min64(kRingStages - 1, nsteps);
+  for (int64_t k = 0; k < pro; ++k) issue(k, (int)k);
+  wait_for(1, pro - 1);
+  __syncthreads();
+  read_slot(0, 0);
+
+  for (int64_t kt = 0; kt < nsteps; ++kt) {
+    const int cur = (int)(kt & 3), nxt = (int)((kt + 1) & 3);
+    if (kt + 3 < nsteps) issue(kt + 3, (int)((kt + 3) & 3));
+    // slot 1 of this step, then slot 0 of the next (on the last step a
+    // harmless read of a stale stage), each under eight matrix instructions
+    read_slot(cur, 1);
+    mma(0, 0, NU);
+    read_slot(nxt, 0);
+    mma(1, 0, NU);
+    __builtin_amdgcn_sched_group_barrier(0x020, LPS, 0);
+#pragma unroll
+    for (int r = 0; r < 2 * NR; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NU - 2 * NR, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_for(kt + 2, min64(kt + 3, nsteps - 1));
+    __syncthreads();
+  }
+
+  // ---- epilogue: bias, round once, masked store (staged through LDS)
+  char *C = (char *)p.C + z * p.strideC * CE;
+  // the loop's last barrier follows every LDS read of the stages
+  static_assert(NW * 32 * stage_pitch<CT, WTN>() <= kRingStages * STAGE, "epilogue staging");
+  store_tile_lds<CT, FM, FN>(acc, lds + wave * 32 * stage_pitch<CT, WTN>(), C, p.ldc, M, N,
+                             m0 + wm * WTM, n0 + wn * WTN, p.bias, 1.f, lane);
+}
+
+template <int AB, int CT, bool NT, int NW>
+hipError_t launch_ring(const GemmParams &p, hipStream_t stream) {
+  const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
+  hipLaunchKernelGGL((gemm_ring_kernel<AB, CT, NT, NW>), dim3((unsigned)tiles), dim3(64 * NW), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace gemm_detail
+}  // namespace tmm

@@ -7,7 +7,8 @@
 // listing; CMU 15-418 Lecture 27 notes, section 7, question 1: about one
 // flop per weight byte).  Matrix instructions would not help; the design
 // goal is enough bytes in flight:
-//   * one wave (64 lanes) owns R consecutive rows; each lane issues all of
+//   * one wave (64 lanes) owns R consecutive rows (R = 1 by default); each
+//     lane issues all of
 //     its 16-byte loads of those rows before using any (8 loads per row for
 //     K = 4096 bf16), so a CU keeps ~128 KiB of W in flight;
 //   * lane l takes chunks l, l+64, ... of a row: every load instruction of a
@@ -16,6 +17,9 @@
 //   * fp32 FMAs, then a 64-lane butterfly sum (the wave analogue of the
 //     warp-shuffle reduction in the Lecture 27 fused-attention listing),
 //     bias, one round-to-nearest-even store.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "tmm_internal.h"
 
 namespace tmm {
@@ -83,15 +87,16 @@ __device__ __forceinline__ void put(void *y, int64_t i, float v) {
   else ((uint16_t *)y)[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
-constexpr int kWaves = 4;  // waves per workgroup
+constexpr int kWaves = 4;  // waves per workgroup of the element path
 constexpr int kUnroll = 8; // 16-byte chunks per lane per row in one pass
 
 // 16-byte path: K*E is a multiple of 16 and W, x, ldw are 16-byte aligned.
-template <int WT, int YT, int R>
-__global__ __launch_bounds__(64 * kWaves) void gemv_vec_kernel(GemvParams p) {
+// WPB waves per workgroup, R rows per wave.
+template <int WT, int YT, int R, int WPB>
+__global__ __launch_bounds__(64 * WPB) void gemv_vec_kernel(GemvParams p) {
   constexpr int E = Bytes<WT>::value;
   const int lane = threadIdx.x & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * R;
+  const int64_t row0 = ((int64_t)blockIdx.x * WPB + (threadIdx.x >> 6)) * R;
   if (row0 >= p.N) return;
   const int64_t nchunks = p.K * E / 16;
   const char *W = (const char *)p.W;
@@ -144,15 +149,43 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_elem_kernel(GemvParams p) {
   if (lane == 0) put<YT>(p.y, row, s + (p.bias ? p.bias[row] : 0.f));
 }
 
-constexpr int kRows = 2;  // rows per wave on the 16-byte path
+template <int WT, int YT, int R, int WPB>
+void launch_vec(const GemvParams &p, hipStream_t stream) {
+  const int64_t waves = (p.N + R - 1) / R;
+  const unsigned blocks = (unsigned)((waves + WPB - 1) / WPB);
+  hipLaunchKernelGGL((gemv_vec_kernel<WT, YT, R, WPB>), dim3(blocks), dim3(64 * WPB), 0, stream, p);
+}
+
+// Rows per wave and waves per workgroup of the 16-byte path.  TMM_GEMV_CFG
+// = "R,W" (R in {1,2,4}, W in {4,8,16}) pins them for measurements.
+int gemv_cfg() {
+  static int cfg = -1;
+  if (cfg < 0) {
+    cfg = 0;
+    const char *s = getenv("TMM_GEMV_CFG");
+    int r = 0, w = 0;
+    if (s && sscanf(s, "%d,%d", &r, &w) == 2 && (r == 1 || r == 2 || r == 4) &&
+        (w == 4 || w == 8 || w == 16))
+      cfg = r * 100 + w;
+  }
+  return cfg;
+}
 
 template <int WT, int YT>
 hipError_t launch_typed(bool vec, const GemvParams &p, hipStream_t stream) {
   if (vec) {
-    const int64_t waves = (p.N + kRows - 1) / kRows;
-    const unsigned blocks = (unsigned)((waves + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((gemv_vec_kernel<WT, YT, kRows>), dim3(blocks), dim3(64 * kWaves), 0,
-                       stream, p);
+    switch (gemv_cfg()) {
+      case 104: launch_vec<WT, YT, 1, 4>(p, stream); break;
+      case 108: launch_vec<WT, YT, 1, 8>(p, stream); break;
+      case 116: launch_vec<WT, YT, 1, 16>(p, stream); break;
+      case 204: launch_vec<WT, YT, 2, 4>(p, stream); break;
+      case 208: launch_vec<WT, YT, 2, 8>(p, stream); break;
+      case 216: launch_vec<WT, YT, 2, 16>(p, stream); break;
+      case 404: launch_vec<WT, YT, 4, 4>(p, stream); break;
+      case 408: launch_vec<WT, YT, 4, 8>(p, stream); break;
+      case 416: launch_vec<WT, YT, 4, 16>(p, stream); break;
+      default: launch_vec<WT, YT, 1, 4>(p, stream); break;
+    }
   } else {
     const unsigned blocks = (unsigned)((p.N + kWaves - 1) / kWaves);
     hipLaunchKernelGGL((gemv_elem_kernel<WT, YT>), dim3(blocks), dim3(64 * kWaves), 0, stream, p);

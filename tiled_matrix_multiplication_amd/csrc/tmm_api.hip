@@ -88,21 +88,22 @@ int cu_count() {
   return cached[dev];
 }
 
-// TMM_FORCE_TILE = "256x256" | "256x128" | "128x128" | "256x256w4" pins the tile shape
-// (for measurements); anything else leaves the choice to pick_tile.
+// TMM_FORCE_TILE = "256x256" | "256x128" | "128x128" | "256x256w4" | "256x256s2" |
+// "256x256r" pins the tile shape for measurements and tile-by-tile tests
+// ("256x256s2": 256x256 tiles on the two-stage kernel only; "256x256r": on
+// the ring kernel wherever it applies, K-contiguous B included).
+// Read on every call so that a test can switch it; anything else leaves the
+// choice to pick_tile.
 int forced_tile() {
-  static int forced = -2;
-  if (forced == -2) {
-    const char *s = getenv("TMM_FORCE_TILE");
-    forced = -1;
-    if (s) {
-      if (!strcmp(s, "256x256")) forced = tmm::kTile256x256;
-      else if (!strcmp(s, "256x128")) forced = tmm::kTile256x128;
-      else if (!strcmp(s, "128x128")) forced = tmm::kTile128x128;
-      else if (!strcmp(s, "256x256w4")) forced = tmm::kTile256x256w4;
-    }
-  }
-  return forced;
+  const char *s = getenv("TMM_FORCE_TILE");
+  if (!s) return -1;
+  if (!strcmp(s, "256x256")) return tmm::kTile256x256;
+  if (!strcmp(s, "256x128")) return tmm::kTile256x128;
+  if (!strcmp(s, "128x128")) return tmm::kTile128x128;
+  if (!strcmp(s, "256x256w4")) return tmm::kTile256x256w4;
+  if (!strcmp(s, "256x256s2")) return tmm::kTile256x256s2;
+  if (!strcmp(s, "256x256r")) return tmm::kTile256x256r;
+  return -1;
 }
 
 // Tile shape with the least estimated time: rounds of `cus` concurrent

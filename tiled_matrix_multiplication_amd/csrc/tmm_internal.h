@@ -18,6 +18,8 @@ enum Tile : int {
   kTile256x128 = 1,
   kTile128x128 = 2,
   kTile256x256w4 = 3,
+  kTile256x256s2 = 4,  // 256x256 on the two-stage kernel only
+  kTile256x256r = 5,   // 256x256 on the ring kernel wherever it applies (also trans_b)
   kNumAutoTiles = 3
 };
 
@@ -36,7 +38,11 @@ struct GemmParams {
 
 // Rows/columns of a workgroup tile.
 inline int tile_bm(Tile t) { return t == kTile128x128 ? 128 : 256; }
-inline int tile_bn(Tile t) { return (t == kTile256x256 || t == kTile256x256w4) ? 256 : 128; }
+inline int tile_bn(Tile t) {
+  return (t == kTile256x256 || t == kTile256x256w4 || t == kTile256x256s2 || t == kTile256x256r)
+             ? 256
+             : 128;
+}
 
 // Launch the tiled MFMA GEMM for one input type with the given tile shape.
 // `vec` selects the 16-byte-load path (every operand row 16-byte aligned);
