@@ -1,6 +1,7 @@
 // Instantiations of the MFMA GEMM kernel for f8 inputs (one translation
 // unit per input type so the kernels build in parallel).
 #include "gemm_mfma.h"
+#include "gemm_ring.h"
 
 namespace tmm {
 

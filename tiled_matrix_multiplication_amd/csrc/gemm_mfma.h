@@ -687,15 +687,22 @@ hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t str
     switch (tile) {
       case kTile256x256:
       case kTile256x256r:
-        // Four-stage ring kernel (gemm_ring.h) for 16-bit inputs and whole
-        // K-steps; chosen automatically for an N-contiguous B, where it
-        // measured faster (with a K-contiguous B the two-stage kernel was).
-        if constexpr (AB == kBF16 || AB == kF16) {
-          if (p.K % 32 == 0 && (!NT || tile == kTile256x256r))
+        // Four-stage ring kernel (gemm_ring.h) for 16-bit and fp8 inputs and
+        // whole 64-byte K-steps; chosen automatically for fp8, and for 16-bit
+        // inputs with an N-contiguous B, where it measured faster (with a
+        // K-contiguous 16-bit B the two-stage kernel was).
+        if constexpr (AB != kF32) {
+          if (p.K % (64 / FmtBytes<AB>::value) == 0 &&
+              (tile == kTile256x256r || !NT || AB == kF8))
             return launch_ring<AB, CT, NT, 8>(p, stream);
         }
+        // the eight-wave two-stage kernel's fp8 fragments do not fit in 256
+        // registers per lane; fp8 takes four waves (accumulators in AGPRs)
+        if constexpr (AB == kF8) return launch_one<AB, CT, NT, 256, 256, 4, true>(p, stream);
         return launch_one<AB, CT, NT, 256, 256, 8, true>(p, stream);
-      case kTile256x256s2: return launch_one<AB, CT, NT, 256, 256, 8, true>(p, stream);
+      case kTile256x256s2:
+        if constexpr (AB == kF8) return launch_one<AB, CT, NT, 256, 256, 4, true>(p, stream);
+        return launch_one<AB, CT, NT, 256, 256, 8, true>(p, stream);
       case kTile256x256w4: return launch_one<AB, CT, NT, 256, 256, 4, true>(p, stream);
       case kTile256x128: return launch_one<AB, CT, NT, 256, 128, 4, true>(p, stream);
       default: return launch_one<AB, CT, NT, 128, 128, 4, true>(p, stream);

@@ -6,7 +6,7 @@
 //
 // Against the two-stage kernel in gemm_mfma.h (which serves every other
 // case), this one keeps global loads three K-steps ahead of their use:
-//   * a K-step is 64 bytes of K per tile row (32 bf16/fp16); a stage
+//   * a K-step is 64 bytes of K per tile row (32 bf16/fp16, 64 fp8); a stage
 //     holds A (256 rows x 64 B) and B (16 KiB), 32 KiB, and four stages fill
 //     128 KiB of the 160 KiB LDS;
 //   * both operands move global->LDS with 16-byte direct loads (no
@@ -20,14 +20,20 @@
 //   * A and a K-contiguous B (trans_b) keep 64-byte rows, chunk c of row r
 //     at position c ^ ((r >> 2) & 3): 16 consecutive rows read at one chunk
 //     fall on 16 distinct bank groups;
-//   * an N-contiguous B (NN, 16-bit types) is stored as it is in memory,
-//     k-rows of BN elements, 16-byte chunk c of row r at c ^ 4 (r & 3), and
-//     the MFMA's B fragments (8 consecutive k of one column per lane) are
-//     read with the gfx950 transposing LDS read ds_read_b64_tr_b16: in a
-//     group of 16 lanes, output lane i, element e is element (i mod 4) of the
-//     8 bytes addressed by lane 4e + i/4, so pointing lane s at k-row
-//     k0 + s/4, columns n0 + 4 (s mod 4) hands lane i the values
-//     B[k0 .. k0+3][n0 + i];
+//   * an N-contiguous B (NN) is stored as it is in memory, k-rows of BN
+//     elements, 16-byte chunk c of row r at c ^ nn_swz(r), and the MFMA's B
+//     fragments (consecutive k of one column per lane) are read with the
+//     gfx950 transposing LDS reads.  ds_read_b64_tr_b16: in a group of 16
+//     lanes, output lane i, element e is element (i mod 4) of the 8 bytes
+//     addressed by lane 4e + i/4, so pointing lane s at k-row k0 + s/4,
+//     columns n0 + 4 (s mod 4) hands lane i B[k0 .. k0+3][n0 + i].
+//     ds_read_b64_tr_b8: output lane i, byte e is byte (i mod 8) of lane
+//     2e + i/8, so lane s at k-row k0 + s/2, columns n0 + 8 (s mod 2) hands
+//     lane i B[k0 .. k0+7][n0 + i] (both layouts measured on gfx950);
+//   * fp8: one 32x32x64 instruction per block and step, fed by both 16-byte
+//     k-slots; the next step's fragments go to a second register set, two
+//     reads after each matrix instruction, the K loop unrolled twice to
+//     swap the sets;
 //   * NW = 8 waves (two per SIMD) each own a 128x64 block of C as 4x2
 //     32x32 accumulators.  NW = 4 (one wave per SIMD, 128x128 blocks as
 //     4x4: a third fewer LDS fragment reads per matrix instruction) also
@@ -42,6 +48,7 @@ namespace gemm_detail {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int kRingStages = 4;
 constexpr int kRingRowBytes = 64;  // bytes of K per tile row per step
@@ -63,11 +70,23 @@ __device__ __forceinline__ uint32_t lds_addr(const char *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
 
-// Transposing 8-byte LDS read (see the header comment).  Kept out of lambdas
-// for the same host-pass reason as load16_to_lds.
+// Transposing 8-byte LDS reads (see the header comment).  Kept out of
+// lambdas for the same host-pass reason as load16_to_lds.
 __device__ __forceinline__ s16x4 lds_read_tr16(const char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4 *)(__attribute__((address_space(3))) char *)p);
+}
+__device__ __forceinline__ i32x2 lds_read_tr8(const char *p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (lds_i32x2 *)(__attribute__((address_space(3))) char *)p);
+}
+
+// NN B stage: 16-byte chunk c of k-row r sits at position c ^ nn_swz(r).
+// The transposing reads take 4 (16-bit) or 8 (8-bit) consecutive k-rows at
+// one chunk; the XOR puts them on distinct bank groups.
+template <int E>
+__device__ __forceinline__ int nn_swz(int row) {
+  return E == 2 ? 4 * (row & 3) : (row & 7);
 }
 
 template <int AB, int CT, bool NT, int NW>
@@ -82,10 +101,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   constexpr int B_BYTES = BN * kRingRowBytes;      // 16 KiB (NT: BN rows x 64 B; NN: BK rows x BN*E B)
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int NB_ROW = BN * E;                   // NN: bytes of one k-row of the B stage
+  constexpr int CPR = NB_ROW / 16, RPI = 64 / CPR; // NN: chunks per k-row, k-rows per load
   constexpr int LA = A_BYTES / 1024 / NW;          // direct loads per wave per step (A)
   constexpr int LB = B_BYTES / 1024 / NW;          // (B)
   constexpr int LPS = LA + LB;
-  static_assert(E == 2, "ring path: 16-bit inputs (fp8 and fp32 use the two-stage kernel)");
+  static_assert(E == 2 || E == 1, "ring path: 16-bit and fp8 inputs (fp32 uses the two-stage kernel)");
   static_assert((NW == 8 || NW == 4) && LA == 16 / NW && LB == 16 / NW, "ring geometry");
 
   __shared__ __attribute__((aligned(16))) char lds[kRingStages * STAGE];
@@ -128,15 +148,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
       b_off[i] = (uint32_t)(r * p.ldb * E + (((lane & 3) ^ swz64(row)) << 4));
     }
   } else {
-    // NN: instruction i of wave w fills k-rows w*4 + 2 i, +1 of the stage
-    // (NB_ROW = 512 bytes each); lane L lands at row L/32, position L%32 and
-    // loads logical chunk (L%32) ^ 4 (row & 3).  A chunk wholly past N (the
-    // host ensures N*E % 16 == 0) reads chunk 0 instead; it only feeds
-    // outputs that are never stored.
+    // NN: k-rows of NB_ROW bytes (CPR chunks); instruction i of wave w
+    // fills the RPI k-rows from w*BK/NW + i*RPI; lane L lands at row L/CPR,
+    // position L%CPR and loads logical chunk (L%CPR) ^ nn_swz(row).  A chunk
+    // wholly past N (the host ensures N*E % 16 == 0) reads chunk 0 instead;
+    // it only feeds outputs that are never stored.
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
-      const int row = wave * (BK / NW) + i * 2 + (lane >> 5);
-      const int c = (lane & 31) ^ (4 * (row & 3));
+      const int row = wave * (BK / NW) + i * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ nn_swz<E>(row);
       const int64_t col = n0 + (int64_t)c * (16 / E);
       const int64_t ccol = col < N ? col : n0;
       b_off[i] = (uint32_t)(((int64_t)row * p.ldb + ccol) * E);
@@ -157,7 +177,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
       if constexpr (NT)
         dma16(bk + b_off[i], la + A_BYTES + (wave * (BN / NW) + i * 16) * kRingRowBytes);
       else
-        dma16(bk + b_off[i], la + A_BYTES + (wave * (BK / NW) + i * 2) * NB_ROW);
+        dma16(bk + b_off[i], la + A_BYTES + (wave * (BK / NW) + i * RPI) * NB_ROW);
     }
   };
 
@@ -202,7 +222,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
           const int row = 16 * s + 4 * h + tr_row0;
           const int col = tr_col0 + 32 * j;                 // element index in the k-row
           const int chunk = (col * E) >> 4, within = (col * E) & 15;
-          h2[h] = lds_read_tr16(base + A_BYTES + row * NB_ROW + ((chunk ^ (4 * (row & 3))) << 4) + within);
+          h2[h] = lds_read_tr16(base + A_BYTES + row * NB_ROW + ((chunk ^ nn_swz<E>(row)) << 4) + within);
         }
         fb[s][j] = i32x4{(int)((uint16_t)h2[0][0] | ((uint32_t)(uint16_t)h2[0][1] << 16)),
                          (int)((uint16_t)h2[0][2] | ((uint32_t)(uint16_t)h2[0][3] << 16)),
@@ -215,7 +235,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
     for (int i = FN; i < FM; ++i) read_a(base, s, i);
   };
 
-  // MFMAs of k-slot s, instructions [u0, u1) of the slot's FM*FN.
+  // MFMAs of k-slot s, instructions [u0, u1) of the slot's FM*FN (16-bit).
   auto mma = [&](int s, int u0, int u1) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = u0; u < u1; ++u) {
@@ -224,13 +244,57 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[s][i]),
                                                             __builtin_bit_cast(bf16x8, fb[s][j]),
                                                             acc[i][j], 0, 0, 0);
-      } else {
+      } else if constexpr (AB == kF16) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[s][i]),
                                                            __builtin_bit_cast(f16x8, fb[s][j]),
                                                            acc[i][j], 0, 0, 0);
       }
     }
   };
+
+  // fp8: a step is one 32x32x64 instruction per block, fed by both k-slots
+  // (chunks g and 2 + g of the 64-byte row: the same k order for A and B).
+  // Fragments live in two register sets, (ca, cb) for this step and
+  // (na, nb) for the next, swapped by unrolling the K loop twice.
+  typedef i32x4 FragA[2][FM];
+  typedef i32x4 FragB[2][FN];
+  auto mma8 = [&](const FragA &ca, const FragB &cb, int i, int j) __attribute__((always_inline)) {
+    const i32x4 a0 = ca[0][i], a1 = ca[1][i], b0 = cb[0][j], b1 = cb[1][j];
+    const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    // format code 0 (fp8 E4M3) for both operands; zero scale operands select
+    // the unscaled instruction
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
+  };
+  // Read number r (0 .. NR8-1) of a step's fragments: first B (NN: four
+  // 8-bit transposing reads per block, piece t holding k 32 (t/2) + 16 g +
+  // 8 (t%2) .. +7 of the lane's column, lane (G, q) of a 16-lane group
+  // pointing at k-row (piece base) + q/2, columns (block) + 16 (G%2) +
+  // 8 (q%2) .. +7; NT: one 16-byte read per slot), then A, one per slot.
+  constexpr int RB8 = FN * (NT ? 2 : 4);
+  constexpr int NR8 = RB8 + 2 * FM;
+  i32x2 pcs[FN][4];
+  auto read8 = [&](int stage, FragA &na, FragB &nb, int r) __attribute__((always_inline)) {
+    const char *base = lds + stage * STAGE;
+    if (r >= RB8) {
+      const int i = (r - RB8) >> 1, s2 = (r - RB8) & 1;
+      na[s2][i] = *(const i32x4 *)(base + a_frag + i * 32 * kRingRowBytes + a_ch[s2]);
+    } else if constexpr (NT) {
+      const int j = r >> 1, s2 = r & 1;
+      nb[s2][j] = *(const i32x4 *)(base + A_BYTES + (wn * WTN + j * 32 + l32) * kRingRowBytes + a_ch[s2]);
+    } else {
+      const int j = r >> 2, t = r & 3;
+      const int row = 32 * (t >> 1) + 16 * g + 8 * (t & 1) + (q >> 1);
+      const int chunk = (wn * WTN + j * 32) / 16 + (G & 1);
+      pcs[j][t] = lds_read_tr8(base + A_BYTES + row * NB_ROW + ((chunk ^ nn_swz<E>(row)) << 4) + 8 * (q & 1));
+      if (t == 3) {
+        nb[0][j] = i32x4{pcs[j][0][0], pcs[j][0][1], pcs[j][1][0], pcs[j][1][1]};
+        nb[1][j] = i32x4{pcs[j][2][0], pcs[j][2][1], pcs[j][3][0], pcs[j][3][1]};
+      }
+    }
+  };
+  FragA fa0, fa1;
+  FragB fb0, fb1;
 
   constexpr int NU = FM * FN;       // MFMAs per k-slot
   constexpr int NR = FM + FN * (NT ? 1 : 2);  // LDS read instructions per slot
@@ -256,35 +320,62 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   for (int64_t k = 0; k < pro; ++k) issue(k, (int)k);
   wait_for(1, pro - 1);
   __syncthreads();
-  read_slot(0, 0);
-
-  for (int64_t kt = 0; kt < nsteps; ++kt) {
-    const int cur = (int)(kt & 3), nxt = (int)((kt + 1) & 3);
-    if (kt + 3 < nsteps) issue(kt + 3, (int)((kt + 3) & 3));
-    // slot 1 of this step, then slot 0 of the next (on the last step a
-    // harmless read of a stale stage), each under eight matrix instructions
-    read_slot(cur, 1);
-    mma(0, 0, NU);
-    read_slot(nxt, 0);
-    mma(1, 0, NU);
-    __builtin_amdgcn_sched_group_barrier(0x020, LPS, 0);
+  if constexpr (E == 1) {
+    // fp8: step kt reads step kt+1's fragments (on the last step a harmless
+    // read of a stale stage) into the other register set, RPM reads after
+    // each matrix instruction, in the order written (scheduling fences).
+    constexpr int RPM = (NR8 + FM * FN - 1) / (FM * FN);
 #pragma unroll
-    for (int r = 0; r < 2 * NR; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int r = 0; r < NR8; ++r) read8(0, fa0, fb0, r);
+    auto step8 = [&](int64_t kt, const FragA &ca, const FragB &cb, FragA &na, FragB &nb)
+        __attribute__((always_inline)) {
+      if (kt + 3 < nsteps) issue(kt + 3, (int)((kt + 3) & 3));
+      const int nxt = (int)((kt + 1) & 3);
+#pragma unroll
+      for (int u = 0; u < FM * FN; ++u) {
+        mma8(ca, cb, u / FN, u % FN);
+#pragma unroll
+        for (int r = u * RPM; r < (u + 1) * RPM && r < NR8; ++r) read8(nxt, na, nb, r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_for(kt + 2, min64(kt + 3, nsteps - 1));
+      __syncthreads();
+    };
+    for (int64_t kt = 0; kt < nsteps; kt += 2) {
+      step8(kt, fa0, fb0, fa1, fb1);
+      if (kt + 1 < nsteps) step8(kt + 1, fa1, fb1, fa0, fb0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NU - 2 * NR, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_for(kt + 2, min64(kt + 3, nsteps - 1));
-    __syncthreads();
+  } else {
+    read_slot(0, 0);
+    for (int64_t kt = 0; kt < nsteps; ++kt) {
+      const int cur = (int)(kt & 3), nxt = (int)((kt + 1) & 3);
+      if (kt + 3 < nsteps) issue(kt + 3, (int)((kt + 3) & 3));
+      // slot 1 of this step, then slot 0 of the next (on the last step a
+      // harmless read of a stale stage), each under eight matrix instructions
+      read_slot(cur, 1);
+      mma(0, 0, NU);
+      read_slot(nxt, 0);
+      mma(1, 0, NU);
+      __builtin_amdgcn_sched_group_barrier(0x020, LPS, 0);
+#pragma unroll
+      for (int r = 0; r < 2 * NR; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NU - 2 * NR, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_for(kt + 2, min64(kt + 3, nsteps - 1));
+      __syncthreads();
+    }
   }
 
-  // ---- epilogue: bias, round once, masked store (staged through LDS)
+  // ---- epilogue: fp8 scale, bias, round once, masked store (staged through LDS)
   char *C = (char *)p.C + z * p.strideC * CE;
   // the loop's last barrier follows every LDS read of the stages
   static_assert(NW * 32 * stage_pitch<CT, WTN>() <= kRingStages * STAGE, "epilogue staging");
   store_tile_lds<CT, FM, FN>(acc, lds + wave * 32 * stage_pitch<CT, WTN>(), C, p.ldc, M, N,
-                             m0 + wm * WTM, n0 + wn * WTN, p.bias, 1.f, lane);
+                             m0 + wm * WTM, n0 + wn * WTN, p.bias, AB == kF8 ? p.scale : 1.f,
+                             lane);
 }
 
 template <int AB, int CT, bool NT, int NW>
