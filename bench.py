@@ -236,7 +236,9 @@ def measure(name, steps, warmup, dev):
     out = {"ms": ms, "wall": wall, "flops": flops, "bytes": nbytes, "copies": copies,
            "sets": sets, "host": host}
     if name == "gemv":
-        out["ms_graph"] = time_graph(run, 100, max(1, steps // 100), warmup)
+        # the eager call is host-bound at this size: time the kernel in a graph
+        out["ms_eager"] = ms
+        out["ms"] = time_graph(run, 100, max(1, steps // 100), warmup)
     return out
 
 
@@ -294,7 +296,7 @@ def _counter_per_dispatch(csv_path, counter, kernel_substr):
 
 
 def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes,
-                  kernel_substr="gemm_mfma_kernel", copy_substr="copy"):
+                  kernel_substr="gemm_", copy_substr="copy"):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the workload's kernel by
     what the same counters read for a plain copy of `copy_bytes` bytes."""
     if name == "gemv":
@@ -441,10 +443,10 @@ def main(argv=None):
     }
     if name == "square_bf16" and not args.no_gemv:
         g = measure("gemv", max(1000, args.steps), max(20, args.warmup), dev)
-        gbs = g["bytes"] / (g["ms_graph"] * 1e-3) / 1e9
-        line["gemv"] = {"workload": describe("gemv"), "us_per_launch": round(g["ms_graph"] * 1e3, 3),
+        gbs = g["bytes"] / (g["ms"] * 1e-3) / 1e9
+        line["gemv"] = {"workload": describe("gemv"), "us_per_launch": round(g["ms"] * 1e3, 3),
                         "timing": "100 launches captured in one HIP graph, replayed",
-                        "us_per_eager_call": round(g["ms"] * 1e3, 3),
+                        "us_per_eager_call": round(g["ms_eager"] * 1e3, 3),
                         "bytes_per_launch": int(g["bytes"]), "achieved": round(gbs, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "weight_copies_rotated": g["copies"], "traffic": traffic_from_profile("gemv")}
