@@ -300,16 +300,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   constexpr int NR = FM + FN * (NT ? 1 : 2);  // LDS read instructions per slot
   // s_waitcnt immediates (gfx9: vmcnt bits 3:0, expcnt 6:4 left at 7,
   // lgkmcnt 11:8 = 0): at most one step's loads left in flight, or none.
+  constexpr int kWait2 = (2 * LPS) | (7 << 4);
   constexpr int kWait1 = LPS | (7 << 4);
   constexpr int kWait0 = 7 << 4;
-  static_assert(LPS < 16, "vmcnt field");
+  static_assert(2 * LPS < 16, "vmcnt field");
 
   // Wait for step `next`'s loads when the newest issued step is `newest`
-  // (never more than one step later).
+  // (at most D - 2 steps later).
   auto wait_for = [&](int64_t next, int64_t newest) __attribute__((always_inline)) {
-    if (newest > next) __builtin_amdgcn_s_waitcnt(kWait1);
+    if (kRingStages > 4 && newest > next + 1) __builtin_amdgcn_s_waitcnt(kWait2);
+    else if (newest > next) __builtin_amdgcn_s_waitcnt(kWait1);
     else __builtin_amdgcn_s_waitcnt(kWait0);
   };
+  constexpr int D = kRingStages - 1;  // steps loaded ahead
+  auto stage_of = [](int64_t k) { return (int)(k % kRingStages); };
 
   const int64_t nsteps = K / BK;  // the host guarantees K % BK == 0, K > 0
   // Barrier b(k), at the end of step k, publishes step k+2: the fragments of
@@ -329,8 +333,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
     for (int r = 0; r < NR8; ++r) read8(0, fa0, fb0, r);
     auto step8 = [&](int64_t kt, const FragA &ca, const FragB &cb, FragA &na, FragB &nb)
         __attribute__((always_inline)) {
-      if (kt + 3 < nsteps) issue(kt + 3, (int)((kt + 3) & 3));
-      const int nxt = (int)((kt + 1) & 3);
+      if (kt + D < nsteps) issue(kt + D, stage_of(kt + D));
+      const int nxt = stage_of(kt + 1);
 #pragma unroll
       for (int u = 0; u < FM * FN; ++u) {
         mma8(ca, cb, u / FN, u % FN);
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
         for (int r = u * RPM; r < (u + 1) * RPM && r < NR8; ++r) read8(nxt, na, nb, r);
         __builtin_amdgcn_sched_barrier(0);
       }
-      wait_for(kt + 2, min64(kt + 3, nsteps - 1));
+      wait_for(kt + 2, min64(kt + D, nsteps - 1));
       __syncthreads();
     };
     for (int64_t kt = 0; kt < nsteps; kt += 2) {
@@ -348,8 +352,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   } else {
     read_slot(0, 0);
     for (int64_t kt = 0; kt < nsteps; ++kt) {
-      const int cur = (int)(kt & 3), nxt = (int)((kt + 1) & 3);
-      if (kt + 3 < nsteps) issue(kt + 3, (int)((kt + 3) & 3));
+      const int cur = stage_of(kt), nxt = stage_of(kt + 1);
+      if (kt + D < nsteps) issue(kt + D, stage_of(kt + D));
       // slot 1 of this step, then slot 0 of the next (on the last step a
       // harmless read of a stale stage), each under eight matrix instructions
       read_slot(cur, 1);
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * NU - 2 * NR, 0);
       __builtin_amdgcn_sched_barrier(0);
-      wait_for(kt + 2, min64(kt + 3, nsteps - 1));
+      wait_for(kt + 2, min64(kt + D, nsteps - 1));
       __syncthreads();
     }
   }
