@@ -30,15 +30,19 @@
 //     ds_read_b64_tr_b8: output lane i, byte e is byte (i mod 8) of lane
 //     2e + i/8, so lane s at k-row k0 + s/2, columns n0 + 8 (s mod 2) hands
 //     lane i B[k0 .. k0+7][n0 + i] (both layouts measured on gfx950);
-//   * fp8: one 32x32x64 instruction per block and step, fed by both 16-byte
-//     k-slots; the next step's fragments go to a second register set, two
-//     reads after each matrix instruction, the K loop unrolled twice to
-//     swap the sets;
+//   * a step's fragments (both 16-byte k-slots of every A and B block) live
+//     in one of two register sets; while the step's matrix instructions
+//     run from one set, the next step's fragments are read into the other,
+//     one or two reads after each instruction in an order fixed by
+//     scheduling fences, the K loop unrolled twice to swap the sets
+//     (16-bit: 16 instructions of 32x32x16 per step, slot-major; fp8: 8 of
+//     32x32x64, each fed by both slots).  This measured 6-10 % faster than
+//     interleaving with sched_group_barrier hints over one register set;
 //   * NW = 8 waves (two per SIMD) each own a 128x64 block of C as 4x2
 //     32x32 accumulators.  NW = 4 (one wave per SIMD, 128x128 blocks as
 //     4x4: a third fewer LDS fragment reads per matrix instruction) also
-//     compiles but measured slower and is not dispatched.  Tile order and
-//     edges as in gemm_mfma.h; the epilogue is store_tile_lds.
+//     compiles but measured much slower and is not dispatched.  Tile order
+//     and edges as in gemm_mfma.h; the epilogue is store_tile_lds.
 #pragma once
 
 #include "gemm_mfma.h"
@@ -54,6 +58,10 @@ constexpr int kRingStages = 4;
 constexpr int kRingRowBytes = 64;  // bytes of K per tile row per step
 
 __device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt(n) in bits 3:0 and 15:14,
+// expcnt left at 7, lgkmcnt(0).
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
 // 16-byte direct global->LDS load: lane L's 16 bytes land at LDS byte
 // address m0 + 16 L.  Written as assembly so that the compiler does not
@@ -203,107 +211,85 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Issue order b0, a0, b1, a1, a2, a3: the first matrix instructions of a
-  // slot (blocks (0,0), (0,1), (1,0), ...) wait for as few reads as possible.
-  i32x4 fa[2][FM], fb[2][FN];
-  auto read_a = [&](const char *base, int s, int i) __attribute__((always_inline)) {
-    fa[s][i] = *(const i32x4 *)(base + a_frag + i * 32 * kRingRowBytes + a_ch[s]);
-  };
-  auto read_slot = [&](int stage, int s) __attribute__((always_inline)) {
-    const char *base = lds + stage * STAGE;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (NT) {
-        fb[s][j] = *(const i32x4 *)(base + A_BYTES + (wn * WTN + j * 32 + l32) * kRingRowBytes + a_ch[s]);
-      } else {
-        s16x4 h2[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = 16 * s + 4 * h + tr_row0;
-          const int col = tr_col0 + 32 * j;                 // element index in the k-row
-          const int chunk = (col * E) >> 4, within = (col * E) & 15;
-          h2[h] = lds_read_tr16(base + A_BYTES + row * NB_ROW + ((chunk ^ nn_swz<E>(row)) << 4) + within);
-        }
-        fb[s][j] = i32x4{(int)((uint16_t)h2[0][0] | ((uint32_t)(uint16_t)h2[0][1] << 16)),
-                         (int)((uint16_t)h2[0][2] | ((uint32_t)(uint16_t)h2[0][3] << 16)),
-                         (int)((uint16_t)h2[1][0] | ((uint32_t)(uint16_t)h2[1][1] << 16)),
-                         (int)((uint16_t)h2[1][2] | ((uint32_t)(uint16_t)h2[1][3] << 16))};
-      }
-      read_a(base, s, j);
-    }
-#pragma unroll
-    for (int i = FN; i < FM; ++i) read_a(base, s, i);
-  };
-
-  // MFMAs of k-slot s, instructions [u0, u1) of the slot's FM*FN (16-bit).
-  auto mma = [&](int s, int u0, int u1) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = u0; u < u1; ++u) {
-      const int i = u / FN, j = u % FN;
-      if constexpr (AB == kBF16) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[s][i]),
-                                                            __builtin_bit_cast(bf16x8, fb[s][j]),
-                                                            acc[i][j], 0, 0, 0);
-      } else if constexpr (AB == kF16) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[s][i]),
-                                                           __builtin_bit_cast(f16x8, fb[s][j]),
-                                                           acc[i][j], 0, 0, 0);
-      }
-    }
-  };
-
-  // fp8: a step is one 32x32x64 instruction per block, fed by both k-slots
-  // (chunks g and 2 + g of the 64-byte row: the same k order for A and B).
-  // Fragments live in two register sets, (ca, cb) for this step and
-  // (na, nb) for the next, swapped by unrolling the K loop twice.
+  // Fenced ping-pong schedule: the fragments of a whole step live in one
+  // of two register sets, (ca, cb)
+  // for this step and (na, nb) for the next, swapped by unrolling the K loop
+  // twice.  fp8: one 32x32x64 instruction per block fed by both k-slots
+  // (chunks g and 2 + g of the 64-byte row: the same k order for A and B);
+  // 16-bit: one 32x32x16 instruction per block and k-slot.
   typedef i32x4 FragA[2][FM];
   typedef i32x4 FragB[2][FN];
-  auto mma8 = [&](const FragA &ca, const FragB &cb, int i, int j) __attribute__((always_inline)) {
-    const i32x4 a0 = ca[0][i], a1 = ca[1][i], b0 = cb[0][j], b1 = cb[1][j];
-    const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-    // format code 0 (fp8 E4M3) for both operands; zero scale operands select
-    // the unscaled instruction
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
+  constexpr int NMS = (E == 1 ? 1 : 2) * FM * FN;  // matrix instructions per step
+  auto mma_u = [&](const FragA &ca, const FragB &cb, int u) __attribute__((always_inline)) {
+    if constexpr (E == 1) {
+      const int i = u / FN, j = u % FN;
+      const i32x4 a0 = ca[0][i], a1 = ca[1][i], b0 = cb[0][j], b1 = cb[1][j];
+      const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      // format code 0 (fp8 E4M3) for both operands; zero scale operands
+      // select the unscaled instruction
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
+    } else {
+      const int s2 = u / (FM * FN), i = (u % (FM * FN)) / FN, j = u % FN;
+      if constexpr (AB == kBF16)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ca[s2][i]),
+                                                            __builtin_bit_cast(bf16x8, cb[s2][j]),
+                                                            acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, ca[s2][i]),
+                                                           __builtin_bit_cast(f16x8, cb[s2][j]),
+                                                           acc[i][j], 0, 0, 0);
+    }
   };
-  // Read number r (0 .. NR8-1) of a step's fragments: first B (NN: four
-  // 8-bit transposing reads per block, piece t holding k 32 (t/2) + 16 g +
-  // 8 (t%2) .. +7 of the lane's column, lane (G, q) of a 16-lane group
-  // pointing at k-row (piece base) + q/2, columns (block) + 16 (G%2) +
-  // 8 (q%2) .. +7; NT: one 16-byte read per slot), then A, one per slot.
-  constexpr int RB8 = FN * (NT ? 2 : 4);
-  constexpr int NR8 = RB8 + 2 * FM;
+  // Read number r (0 .. NRS-1) of a step's fragments: first B, then A (one
+  // 16-byte read per slot and block).  B, NT: one 16-byte read per slot.
+  // B, NN, fp8: four 8-bit transposing reads per block, piece t holding
+  // k 32 (t/2) + 16 g + 8 (t%2) .. +7 of the lane's column (lane (G, q) of a
+  // 16-lane group points at k-row (piece base) + q/2, columns (block) +
+  // 16 (G%2) + 8 (q%2) .. +7).  B, NN, 16-bit: four 16-bit transposing
+  // reads per block, piece t = 2 s + h holding k 16 s + 8 g + 4 h .. +3.
+  constexpr int RBS = FN * (NT ? 2 : 4);
+  constexpr int NRS = RBS + 2 * FM;
   i32x2 pcs[FN][4];
-  auto read8 = [&](int stage, FragA &na, FragB &nb, int r) __attribute__((always_inline)) {
+  auto read_r = [&](int stage, FragA &na, FragB &nb, int r) __attribute__((always_inline)) {
     const char *base = lds + stage * STAGE;
-    if (r >= RB8) {
-      const int i = (r - RB8) >> 1, s2 = (r - RB8) & 1;
+    if (r >= RBS) {
+      const int i = (r - RBS) >> 1, s2 = (r - RBS) & 1;
       na[s2][i] = *(const i32x4 *)(base + a_frag + i * 32 * kRingRowBytes + a_ch[s2]);
     } else if constexpr (NT) {
       const int j = r >> 1, s2 = r & 1;
       nb[s2][j] = *(const i32x4 *)(base + A_BYTES + (wn * WTN + j * 32 + l32) * kRingRowBytes + a_ch[s2]);
     } else {
       const int j = r >> 2, t = r & 3;
-      const int row = 32 * (t >> 1) + 16 * g + 8 * (t & 1) + (q >> 1);
-      const int chunk = (wn * WTN + j * 32) / 16 + (G & 1);
-      pcs[j][t] = lds_read_tr8(base + A_BYTES + row * NB_ROW + ((chunk ^ nn_swz<E>(row)) << 4) + 8 * (q & 1));
-      if (t == 3) {
-        nb[0][j] = i32x4{pcs[j][0][0], pcs[j][0][1], pcs[j][1][0], pcs[j][1][1]};
-        nb[1][j] = i32x4{pcs[j][2][0], pcs[j][2][1], pcs[j][3][0], pcs[j][3][1]};
+      if constexpr (E == 1) {
+        const int row = 32 * (t >> 1) + 16 * g + 8 * (t & 1) + (q >> 1);
+        const int chunk = (wn * WTN + j * 32) / 16 + (G & 1);
+        pcs[j][t] = lds_read_tr8(base + A_BYTES + row * NB_ROW + ((chunk ^ nn_swz<E>(row)) << 4) + 8 * (q & 1));
+        if (t == 3) {
+          nb[0][j] = i32x4{pcs[j][0][0], pcs[j][0][1], pcs[j][1][0], pcs[j][1][1]};
+          nb[1][j] = i32x4{pcs[j][2][0], pcs[j][2][1], pcs[j][3][0], pcs[j][3][1]};
+        }
+      } else {
+        const int row = 16 * (t >> 1) + 4 * (t & 1) + tr_row0;
+        const int col = tr_col0 + 32 * j;
+        const int chunk = (col * E) >> 4, within = (col * E) & 15;
+        pcs[j][t] = __builtin_bit_cast(
+            i32x2, lds_read_tr16(base + A_BYTES + row * NB_ROW + ((chunk ^ nn_swz<E>(row)) << 4) + within));
+        if (t & 1) {
+          const int s2 = t >> 1;
+          nb[s2][j] = i32x4{pcs[j][t - 1][0], pcs[j][t - 1][1], pcs[j][t][0], pcs[j][t][1]};
+        }
       }
     }
   };
   FragA fa0, fa1;
   FragB fb0, fb1;
 
-  constexpr int NU = FM * FN;       // MFMAs per k-slot
-  constexpr int NR = FM + FN * (NT ? 1 : 2);  // LDS read instructions per slot
-  // s_waitcnt immediates (gfx9: vmcnt bits 3:0, expcnt 6:4 left at 7,
-  // lgkmcnt 11:8 = 0): at most one step's loads left in flight, or none.
-  constexpr int kWait2 = (2 * LPS) | (7 << 4);
-  constexpr int kWait1 = LPS | (7 << 4);
-  constexpr int kWait0 = 7 << 4;
-  static_assert(2 * LPS < 16, "vmcnt field");
+  // waits that leave at most two, one or no step's loads in flight
+  constexpr int kWait2 = vm_wait(2 * LPS);
+  constexpr int kWait1 = vm_wait(LPS);
+  constexpr int kWait0 = vm_wait(0);
+  static_assert(2 * LPS < 64, "vmcnt field");
 
   // Wait for step `next`'s loads when the newest issued step is `newest`
   // (at most D - 2 steps later).
@@ -318,58 +304,36 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   const int64_t nsteps = K / BK;  // the host guarantees K % BK == 0, K > 0
   // Barrier b(k), at the end of step k, publishes step k+2: the fragments of
   // step k+1 can then be read during step k, under its matrix instructions,
-  // and no LDS read waits behind a barrier.  Stage (k+3) mod 4, which step k
+  // and no LDS read waits behind a barrier.  Stage (k+D) mod S, which step k
   // loads, was last read during step k-1, before b(k-1).
   const int64_t pro = min64(kRingStages - 1, nsteps);
   for (int64_t k = 0; k < pro; ++k) issue(k, (int)k);
   wait_for(1, pro - 1);
   __syncthreads();
-  if constexpr (E == 1) {
-    // fp8: step kt reads step kt+1's fragments (on the last step a harmless
-    // read of a stale stage) into the other register set, RPM reads after
-    // each matrix instruction, in the order written (scheduling fences).
-    constexpr int RPM = (NR8 + FM * FN - 1) / (FM * FN);
+  {
+    // Step kt reads step kt+1's fragments (on the last step a harmless read
+    // of a stale stage) into the other register set, RPM reads after each
+    // matrix instruction, in the order written (scheduling fences).
+    constexpr int RPM = (NRS + NMS - 1) / NMS;
 #pragma unroll
-    for (int r = 0; r < NR8; ++r) read8(0, fa0, fb0, r);
-    auto step8 = [&](int64_t kt, const FragA &ca, const FragB &cb, FragA &na, FragB &nb)
+    for (int r = 0; r < NRS; ++r) read_r(0, fa0, fb0, r);
+    auto step_f = [&](int64_t kt, const FragA &ca, const FragB &cb, FragA &na, FragB &nb)
         __attribute__((always_inline)) {
       if (kt + D < nsteps) issue(kt + D, stage_of(kt + D));
       const int nxt = stage_of(kt + 1);
 #pragma unroll
-      for (int u = 0; u < FM * FN; ++u) {
-        mma8(ca, cb, u / FN, u % FN);
+      for (int u = 0; u < NMS; ++u) {
+        mma_u(ca, cb, u);
 #pragma unroll
-        for (int r = u * RPM; r < (u + 1) * RPM && r < NR8; ++r) read8(nxt, na, nb, r);
+        for (int r = u * RPM; r < (u + 1) * RPM && r < NRS; ++r) read_r(nxt, na, nb, r);
         __builtin_amdgcn_sched_barrier(0);
       }
       wait_for(kt + 2, min64(kt + D, nsteps - 1));
       __syncthreads();
     };
     for (int64_t kt = 0; kt < nsteps; kt += 2) {
-      step8(kt, fa0, fb0, fa1, fb1);
-      if (kt + 1 < nsteps) step8(kt + 1, fa1, fb1, fa0, fb0);
-    }
-  } else {
-    read_slot(0, 0);
-    for (int64_t kt = 0; kt < nsteps; ++kt) {
-      const int cur = stage_of(kt), nxt = stage_of(kt + 1);
-      if (kt + D < nsteps) issue(kt + D, stage_of(kt + D));
-      // slot 1 of this step, then slot 0 of the next (on the last step a
-      // harmless read of a stale stage), each under eight matrix instructions
-      read_slot(cur, 1);
-      mma(0, 0, NU);
-      read_slot(nxt, 0);
-      mma(1, 0, NU);
-      __builtin_amdgcn_sched_group_barrier(0x020, LPS, 0);
-#pragma unroll
-      for (int r = 0; r < 2 * NR; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NU - 2 * NR, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      wait_for(kt + 2, min64(kt + D, nsteps - 1));
-      __syncthreads();
+      step_f(kt, fa0, fb0, fa1, fb1);
+      if (kt + 1 < nsteps) step_f(kt + 1, fa1, fb1, fa0, fb0);
     }
   }
 
