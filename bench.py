@@ -154,9 +154,30 @@ def launcher(name, sets, dbias, sa, sb):
     return run
 
 
-def time_steps(run, steps, warmup):
-    """Average ms per launch from HIP events on the launching (current) stream."""
+SETTLE_S = 0.15
+
+
+def settle(run):
+    """Keep the GPU busy for SETTLE_S seconds of wall time before anything is
+    timed: from idle, the chip's clock ramps up over the first ~30 ms of
+    sustained load (4096^3 bf16: 155 us per launch at first, 125 us after
+    ~30 ms), so a short warmup would time the ramp rather than the kernel."""
     import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < SETTLE_S and i < 100000:
+        for _ in range(8):
+            run(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
+def time_steps(run, steps, warmup):
+    """Average ms per launch from HIP events on the launching (current) stream,
+    after the clock has settled and `warmup` untimed launches."""
+    import torch
+    settle(run)
     for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
@@ -182,6 +203,7 @@ def time_graph(run, launches, replays, warmup):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
+        settle(run)
         for i in range(warmup):
             run(i)
     torch.cuda.current_stream().wait_stream(side)

@@ -216,7 +216,8 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[FM][FN], char
       if (grow >= M || gcol >= N) continue;
       char *dst = C + (grow * ldc + gcol) * CE;
       if (vec && gcol + EPC <= N) {
-        *(i32x4 *)dst = v;
+        // non-temporal: C is written once and not read back here
+        __builtin_nontemporal_store(v, (i32x4 *)dst);
       } else {
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
