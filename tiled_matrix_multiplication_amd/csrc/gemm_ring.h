@@ -312,9 +312,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   __syncthreads();
   {
     // Step kt reads step kt+1's fragments (on the last step a harmless read
-    // of a stale stage) into the other register set, RPM reads after each
-    // matrix instruction, in the order written (scheduling fences).
-    constexpr int RPM = (NRS + NMS - 1) / NMS;
+    // of a stale stage) into the other register set, RPM reads after each of
+    // the first three quarters of the matrix instructions (so the reads have
+    // landed when the barrier's lgkmcnt(0) comes), in the order written
+    // (scheduling fences).
+    constexpr int RW = NMS - NMS / 4;
+    constexpr int RPM = (NRS + RW - 1) / RW;
 #pragma unroll
     for (int r = 0; r < NRS; ++r) read_r(0, fa0, fb0, r);
     auto step_f = [&](int64_t kt, const FragA &ca, const FragB &cb, FragA &na, FragB &nb)
