@@ -1,17 +1,20 @@
 """The oracle: TEST INFRASTRUCTURE ONLY.
 
 A plain fp64 CPU statement of C = s_a*s_b * A . op(B) (+ bias) over the
-exactly decoded low-precision inputs, plus the format decoders and the
-round-to-nearest-even encoders it needs (all in ``oracle.c``).
+exactly decoded low-precision inputs, of one attention head
+o = softmax(scale * Q . K^T) . V, plus the format decoders and the
+round-to-nearest-even encoders they need (all in ``oracle.c``).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It shares no code with the HIP
 library (``tiled_matrix_multiplication_amd``) and never imports it.
 
-Every function here is pinned by ``tests/test_oracle.py`` against facts that
-do not come from the oracle itself (brute force, closed forms, the block
-decomposition identity of the "GEMM to FlashAttention" page's tiling figure,
-and independent library conversions for the codecs).
+Every function here is pinned by ``tests/test_oracle.py`` and
+``tests/test_oracle_attention.py`` against facts that do not come from the
+oracle itself (brute force, closed forms, the block decomposition identity of
+the "GEMM to FlashAttention" page's tiling figure, independent library
+conversions for the codecs, an independent softmax routine and the
+invariances of softmax for the attention).
 """
 from __future__ import annotations
 
@@ -58,7 +61,10 @@ def _load():
     lib.oracle_gemm.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, vp, i64,
                                 ctypes.c_int, vp, dp, dp, vp, i64, vp]
     lib.oracle_threads.argtypes = []
-    for f in (lib.oracle_decode, lib.oracle_round, lib.oracle_gemm, lib.oracle_threads):
+    lib.oracle_attention.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, vp, i64, vp, i64,
+                                     ctypes.c_double, vp, i64, vp]
+    for f in (lib.oracle_decode, lib.oracle_round, lib.oracle_gemm, lib.oracle_threads,
+              lib.oracle_attention):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -134,6 +140,33 @@ def gemm(fmt, A: np.ndarray, B: np.ndarray, trans_b: bool = False,
     if rc:
         raise ValueError(f"oracle_gemm failed ({rc})")
     return (C, T) if want_abs else C
+
+
+def attention(fmt, Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+              want_abs: bool = False):
+    """o = softmax(scale * Q . K^T) . V in float64, one head.
+
+    Q: (Nq, D), K and V: (Nk, D) bit patterns of ``fmt`` (row strides are
+    honoured).  Returns o (Nq, D) float64, and with ``want_abs`` also
+    T[i][c] = sum_j w_ij |v_jc| (same shape).
+    """
+    f = _fmt(fmt)
+    arrs = [_rowmajor(np.asarray(X)) for X in (Q, K, V)]
+    if any(X.dtype != _BITS[f] or X.ndim != 2 for X in arrs):
+        raise TypeError("Q, K and V must be 2-D arrays of the format's bit patterns")
+    Q, K, V = arrs
+    Nq, D = Q.shape
+    Nk = K.shape[0]
+    if K.shape[1] != D or V.shape != (Nk, D):
+        raise ValueError(f"shapes differ: Q {Q.shape}, K {K.shape}, V {V.shape}")
+    ld = [X.strides[0] // X.itemsize if X.shape[0] > 1 else D for X in (Q, K, V)]
+    O = np.empty((Nq, D), dtype=np.float64)
+    T = np.empty((Nq, D), dtype=np.float64) if want_abs else None
+    rc = _load().oracle_attention(Nq, Nk, D, f, _ptr(Q), ld[0], _ptr(K), ld[1], _ptr(V), ld[2],
+                                  float(scale), _ptr(O), D, _ptr(T))
+    if rc:
+        raise ValueError(f"oracle_attention failed ({rc})")
+    return (O, T) if want_abs else O
 
 
 def threads() -> int:

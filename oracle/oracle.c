@@ -34,6 +34,8 @@
  * value, ties to the even significand", written from that definition on the
  * format's grid of representable values.
  *
+ * oracle_attention states softmax(scale Q K^T) V the same way (see there).
+ *
  * Each pin of this file lives in tests/test_oracle.py.
  */
 #include <math.h>
@@ -265,6 +267,81 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int fmt, const void *A,
     free(tab);
   }
   free(bp);
+  return fail ? -3 : 0;
+}
+
+/*
+ * Scaled dot-product attention of one head, in double precision:
+ *
+ *   s[i][j] = scale * sum_{c<D} q[i][c] * k[j][c]
+ *   w[i][j] = exp(s[i][j]) / sum_{j'<Nk} exp(s[i][j'])   (softmax over keys)
+ *   o[i][c] = sum_{j<Nk} w[i][j] * v[j][c]
+ *
+ * "GEMM to FlashAttention" page (youngju.dev): the attention formula at its
+ * top and the attention_standard listing (scores Q K^T times a scale that
+ * defaults to 1/sqrt(d), softmax over the last axis, then times V).  The
+ * exponentials are taken of s - max_j s, the same quotient written so that
+ * exp cannot overflow.
+ *
+ *   Q  : Nq rows of D inputs (format fmt) at stride ldq
+ *   K  : Nk rows of D inputs at stride ldk
+ *   V  : Nk rows of D inputs at stride ldv
+ *   O  : Nq rows of D doubles at stride ldo (written)
+ *   T  : NULL or like O, T[i][c] = sum_j w[i][j] |v[j][c]| (the scale of
+ *        the error of any evaluation that rounds the weights)
+ *
+ * Rows are independent and spread over OpenMP threads.
+ */
+int oracle_attention(int64_t Nq, int64_t Nk, int64_t D, int fmt, const void *Q,
+                     int64_t ldq, const void *K, int64_t ldk, const void *V,
+                     int64_t ldv, double scale, double *O, int64_t ldo, double *T) {
+  if (Nq < 0 || Nk < 1 || D < 1 || fmt < ORC_F32 || fmt > ORC_E4M3)
+    return -1;
+  if (ldq < D || ldk < D || ldv < D || ldo < D)
+    return -2;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double *q = (double *)malloc(sizeof(double) * (size_t)D);
+    double *s = (double *)malloc(sizeof(double) * (size_t)Nk);
+    if (!q || !s) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t i = 0; i < Nq; ++i) {
+        for (int64_t c = 0; c < D; ++c)
+          q[c] = dec_at(fmt, Q, i * ldq + c);
+        double smax = -HUGE_VAL;
+        for (int64_t j = 0; j < Nk; ++j) {
+          double dot = 0.0;
+          for (int64_t c = 0; c < D; ++c)
+            dot += q[c] * dec_at(fmt, K, j * ldk + c);
+          s[j] = scale * dot;
+          if (s[j] > smax)
+            smax = s[j];
+        }
+        double den = 0.0;
+        for (int64_t j = 0; j < Nk; ++j) {
+          s[j] = exp(s[j] - smax); /* s now holds the unnormalised weights */
+          den += s[j];
+        }
+        for (int64_t c = 0; c < D; ++c) {
+          double acc = 0.0, tab = 0.0;
+          for (int64_t j = 0; j < Nk; ++j) {
+            const double v = dec_at(fmt, V, j * ldv + c);
+            acc += s[j] * v;
+            tab += s[j] * fabs(v);
+          }
+          O[i * ldo + c] = acc / den;
+          if (T)
+            T[i * ldo + c] = tab / den;
+        }
+      }
+    }
+    free(q);
+    free(s);
+  }
   return fail ? -3 : 0;
 }
 
