@@ -134,6 +134,33 @@ int tmm_gemv(int64_t N, int64_t K, tmm_dtype w_type, tmm_dtype y_type,
              const void *W, int64_t ldw, const void *x, void *y,
              const float *bias, hipStream_t stream);
 
+/*
+ * Fused attention forward, one head per batch entry z < batch:
+ *   O[z][i][c] = sum_j w[i][j] V[z][j][c],
+ *   w[i][j] = exp(s[i][j]) / sum_j' exp(s[i][j']),   s = scale * Q[z] . K[z]^T
+ * ("GEMM to FlashAttention" page: the attention formula and the
+ * attention_standard listing, whose scale defaults to 1/sqrt(D); evaluated
+ * with the online softmax of its flash_attention_simplified listing, so the
+ * Nq x Nk scores never reach memory).  No mask.
+ *   Q : Nq x D rows at ldq, K and V : Nk x D rows at ldk / ldv, O : Nq x D
+ *   rows at ldo; batch strides in elements, >= 0 (the O matrices must not
+ *   overlap: strideO >= (Nq-1)*ldo + D when batch > 1).
+ *   in_type: TMM_F16 or TMM_BF16 (Q, K, V alike); out_type: in_type or
+ *   TMM_F32.  Scores and sums are fp32; the weights enter the second product
+ *   rounded to in_type.
+ *   D must be 64 or 128 (TMM_ERR_DIM otherwise); Nk >= 1 when Nq > 0
+ *   (TMM_ERR_DIM); every pointer 16-byte aligned and every ld and stride a
+ *   multiple of 8 elements (TMM_ERR_ALIGN); scale finite (TMM_ERR_SCALE).
+ * Quick return: batch == 0 or Nq == 0.
+ */
+int tmm_attention_fwd(int64_t batch, int64_t Nq, int64_t Nk, int64_t D,
+                      tmm_dtype in_type, tmm_dtype out_type,
+                      const void *Q, int64_t ldq, int64_t strideQ,
+                      const void *K, int64_t ldk, int64_t strideK,
+                      const void *V, int64_t ldv, int64_t strideV,
+                      void *O, int64_t ldo, int64_t strideO, float scale,
+                      hipStream_t stream);
+
 /* Static English text of a status code (never NULL). */
 const char *tmm_status_string(int status);
 

@@ -24,7 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemv", "tmm_status_string", "tmm_version"])
+        ["tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemv", "tmm_attention_fwd",
+         "tmm_status_string", "tmm_version"])
 
 
 def test_library_exports_every_declared_symbol(tmm):
@@ -128,3 +129,36 @@ def test_binding_rejects_host_tensors(tmm):
 def test_operand_span_limit(tmm):
     # 65536 x 32769 bf16 = 4 GiB + 128 KiB: rejected before any HIP call
     assert gemm(tmm, M=65536, N=64, K=32769) == -1
+
+
+def attn(tmm, Z=2, Nq=64, Nk=64, D=128, it=2, ot=2, Q=FAKE, K=FAKE2, V=FAKE3, O=FAKE, ld=None,
+         ldo=None, sq=None, so=None, scale=0.1):
+    ld = D if ld is None else ld
+    ldo = D if ldo is None else ldo
+    sq = Nq * ld if sq is None else sq
+    so = Nq * ldo if so is None else so
+    return tmm.lib.tmm_attention_fwd(Z, Nq, Nk, D, it, ot, Q, ld, sq, K, ld, Nk * ld, V, ld, Nk * ld,
+                                     O, ldo, so, scale, None)
+
+
+def test_attention_validation(tmm):
+    """Every bad argument is refused on the host with its code; the pointers
+    are fake, so a call that passed validation would be a failure here too."""
+    assert attn(tmm, D=96) == -1                      # D must be 64 or 128
+    assert attn(tmm, Nq=-1) == -1
+    assert attn(tmm, Nk=0) == -1                      # softmax over no keys
+    assert attn(tmm, it=0, ot=0) == -4                # fp32 inputs are not accepted
+    assert attn(tmm, it=3, ot=1) == -4                # nor fp8
+    assert attn(tmm, it=2, ot=1) == -4                # f16 -> bf16 is not a pair
+    assert attn(tmm, ld=64) == -2                     # ld below D
+    assert attn(tmm, so=64 * 128 - 1) == -6           # O matrices overlap
+    assert attn(tmm, scale=float("inf")) == -5
+    assert attn(tmm, Q=None) == -3
+    assert attn(tmm, ld=132, sq=64 * 132) == -7       # ld not a multiple of 8
+    assert attn(tmm, Q=ctypes.c_void_p(0x100008)) == -7   # not 16-byte aligned
+
+
+def test_attention_quick_returns(tmm):
+    """batch == 0 or Nq == 0 enqueue nothing (NULL pointers are then fine)."""
+    assert attn(tmm, Z=0, Q=None, K=None, V=None, O=None) == 0
+    assert attn(tmm, Nq=0, Q=None, K=None, V=None, O=None) == 0

@@ -24,7 +24,8 @@ STATUS = {
     -5: "TMM_ERR_SCALE", -6: "TMM_ERR_STRIDE", -7: "TMM_ERR_ALIGN", -8: "TMM_ERR_LAUNCH",
 }
 
-EXPORTS = ("tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemv", "tmm_status_string", "tmm_version")
+EXPORTS = ("tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemv", "tmm_attention_fwd",
+           "tmm_status_string", "tmm_version")
 
 _DTYPE = {torch.float32: TMM_F32, torch.bfloat16: TMM_BF16, torch.float16: TMM_F16,
           torch.float8_e4m3fn: TMM_F8E4M3}
@@ -46,10 +47,13 @@ def _load() -> ctypes.CDLL:
     lib.tmm_gemm_strided_batched.argtypes = [i64, i64, i64, ci, ci, ci, vp, i64, i64, vp, i64, i64,
                                              vp, i64, i64, i64, vp, cf, cf, vp]
     lib.tmm_gemv.argtypes = [i64, i64, ci, ci, vp, i64, vp, vp, vp, vp]
+    lib.tmm_attention_fwd.argtypes = [i64, i64, i64, i64, ci, ci, vp, i64, i64, vp, i64, i64,
+                                      vp, i64, i64, vp, i64, i64, cf, vp]
     lib.tmm_status_string.argtypes = [ci]
     lib.tmm_status_string.restype = ctypes.c_char_p
     lib.tmm_version.argtypes = []
-    for f in (lib.tmm_gemm, lib.tmm_gemm_strided_batched, lib.tmm_gemv, lib.tmm_version):
+    for f in (lib.tmm_gemm, lib.tmm_gemm_strided_batched, lib.tmm_gemv, lib.tmm_attention_fwd,
+              lib.tmm_version):
         f.restype = ci
     return lib
 
@@ -161,3 +165,25 @@ def tmm_gemv(W: torch.Tensor, x: torch.Tensor, y: torch.Tensor, bias: torch.Tens
                       ctypes.c_void_p(_stream(stream)))
     _check("tmm_gemv", rc)
     return y
+
+
+def tmm_attention_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor,
+                      scale: float | None = None, stream=None):
+    """O[z] = softmax(scale * Q[z] . K[z]^T) . V[z] for 3-D tensors (batch, rows, D);
+    scale defaults to 1/sqrt(D)."""
+    _on_gpu(Q, K, V, O)
+    Z, Nq, D = Q.shape
+    Nk = K.shape[1]
+    if tuple(K.shape) != (Z, Nk, D) or tuple(V.shape) != (Z, Nk, D) or tuple(O.shape) != (Z, Nq, D):
+        raise ValueError(f"shape mismatch: Q {tuple(Q.shape)}, K {tuple(K.shape)}, "
+                         f"V {tuple(V.shape)}, O {tuple(O.shape)}")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K and V must have the same element type")
+    if scale is None:
+        scale = float(D) ** -0.5
+    rc = lib.tmm_attention_fwd(Z, Nq, Nk, D, _dtype(Q), _dtype(O), _ptr(Q), _ld(Q), int(Q.stride(0)),
+                               _ptr(K), _ld(K), int(K.stride(0)), _ptr(V), _ld(V), int(V.stride(0)),
+                               _ptr(O), _ld(O), int(O.stride(0)), float(scale),
+                               ctypes.c_void_p(_stream(stream)))
+    _check("tmm_attention_fwd", rc)
+    return O

@@ -234,6 +234,38 @@ int tmm_gemv(int64_t N, int64_t K, tmm_dtype w_type, tmm_dtype y_type, const voi
   return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
 }
 
+int tmm_attention_fwd(int64_t batch, int64_t Nq, int64_t Nk, int64_t D, tmm_dtype in_type,
+                      tmm_dtype out_type, const void *Q, int64_t ldq, int64_t strideQ,
+                      const void *K, int64_t ldk, int64_t strideK, const void *V, int64_t ldv,
+                      int64_t strideV, void *O, int64_t ldo, int64_t strideO, float scale,
+                      hipStream_t stream) {
+  if (batch < 0 || Nq < 0 || Nk < 0 || (D != 64 && D != 128)) return TMM_ERR_DIM;
+  if ((in_type != TMM_F16 && in_type != TMM_BF16) ||
+      (out_type != in_type && out_type != TMM_F32))
+    return TMM_ERR_DTYPE;
+  if (ldq < D || ldk < D || ldv < D || ldo < D) return TMM_ERR_LD;
+  if (strideQ < 0 || strideK < 0 || strideV < 0 || strideO < 0) return TMM_ERR_STRIDE;
+  if (batch > 1 && Nq > 0 && strideO < (Nq - 1) * ldo + D) return TMM_ERR_STRIDE;
+  if (!isfinite(scale)) return TMM_ERR_SCALE;
+  if (batch == 0 || Nq == 0) return TMM_OK;
+  if (Nk == 0) return TMM_ERR_DIM;  // softmax over no keys
+  if (!Q || !K || !V || !O) return TMM_ERR_NULL;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || ldq % 8 ||
+      ldk % 8 || ldv % 8 || ldo % 8 || strideQ % 8 || strideK % 8 || strideV % 8 || strideO % 8)
+    return TMM_ERR_ALIGN;
+  if (batch * ((Nq + 127) / 128) >= ((int64_t)1 << 31)) return TMM_ERR_DIM;
+
+  tmm::AttnParams p;
+  p.Z = batch; p.Nq = Nq; p.Nk = Nk;
+  p.Q = Q; p.ldq = ldq; p.strideQ = strideQ;
+  p.K = K; p.ldk = ldk; p.strideK = strideK;
+  p.V = V; p.ldv = ldv; p.strideV = strideV;
+  p.O = O; p.ldo = ldo; p.strideO = strideO;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t err = tmm::launch_attention((Fmt)in_type, (Fmt)out_type, (int)D, p, stream);
+  return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
+}
+
 const char *tmm_status_string(int status) {
   switch (status) {
     case TMM_OK: return "success";

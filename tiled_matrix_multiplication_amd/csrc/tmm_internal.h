@@ -71,4 +71,21 @@ struct GemvParams {
 
 hipError_t launch_gemv(Fmt w, Fmt y, bool vec, const GemvParams &p, hipStream_t stream);
 
+struct AttnParams {
+  int64_t Z, Nq, Nk;
+  const void *Q;
+  int64_t ldq, strideQ;
+  const void *K;
+  int64_t ldk, strideK;
+  const void *V;
+  int64_t ldv, strideV;
+  void *O;
+  int64_t ldo, strideO;
+  float scale_log2;  // scale * log2(e): scores go through exp2
+};
+
+// Fused attention forward (attention.hip); D is 64 or 128, in is kF16 or
+// kBF16, out is in or kF32 (the host has checked all of it).
+hipError_t launch_attention(Fmt in, Fmt out, int D, const AttnParams &p, hipStream_t stream);
+
 }  // namespace tmm
