@@ -88,7 +88,29 @@ WORKLOADS = {
     "ragged_4097x511x1023": (4097, 511, 1023, 1, "bf16", "bf16", False, False),
     "f32_256": (256, 256, 256, 1, "f32", "f32", False, False),
     "gemv": (1, 4096, 4096, 1, "bf16", "bf16", True, True),
+    # fused attention: (Nq queries, Nk keys, D head size, batch x heads, in, out, -, -)
+    "attn_fused": (2048, 2048, 128, 128, "f16", "f16", True, False),
 }
+
+ATTENTION = ("attn_fused",)
+
+
+def attention_flops(Nq, Nk, D, batch=1):
+    """Two products per head, S = Q K^T and O = P V: 2 Nq Nk D each."""
+    return 4.0 * Nq * Nk * D * batch
+
+
+def attention_bytes(Nq, Nk, D, in_bytes, out_bytes, batch=1):
+    """Compulsory traffic: read Q, K and V once, write O once."""
+    return float(batch * ((Nq + 2 * Nk) * D * in_bytes + Nq * D * out_bytes))
+
+
+def work(name):
+    """(algorithmic flops, algorithmic bytes) of one launch of a workload."""
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    if name in ATTENTION:
+        return attention_flops(M, N, K, Z), attention_bytes(M, N, K, BYTES[fin], BYTES[fout], Z)
+    return gemm_flops(M, N, K, Z), gemm_bytes(M, N, K, BYTES[fin], BYTES[fout], Z, bias)
 
 
 def describe(name):
@@ -97,6 +119,9 @@ def describe(name):
     b = f"batch {Z} x " if Z > 1 else ""
     if name == "gemv":
         return f"{fin} GEMV y = W.x + bias, W {N}x{K}, {fout} y"
+    if name in ATTENTION:
+        return (f"{fin} fused attention softmax(Q K^T/sqrt(D)) V, batch x heads {Z}, "
+                f"{M} queries x {N} keys, head size {K}, {fout} out")
     return f"{fin} GEMM {b}{M}x{N}x{K} {lay}, {fout} out{', fp32 bias' if bias else ''}"
 
 
@@ -106,6 +131,15 @@ def make_inputs(name, copies, dev):
 
     import synthetic as syn
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    if name in ATTENTION:
+        # N(0,1) Q, K, V of batch x heads independent heads (the attention shapes)
+        Q, Kt, V = (syn.to_bits(syn.normal(shape, syn.seed_of(6, t)), fin)
+                    for t, shape in (("A", (Z, M, K)), ("B", (Z, N, K)), ("V", (Z, N, K))))
+        hQ, hK, hV = (syn.as_torch(X, fin) for X in (Q, Kt, V))
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[fout]
+        sets = [(hQ.to(dev), hK.to(dev), hV.to(dev), torch.empty((Z, M, K), dtype=tdt, device=dev))
+                for _ in range(copies)]
+        return sets, None, (Q, Kt, V, 1.0, 1.0)
     cfg = {"square_bf16": 2, "qkv": 3, "ffn_up": 3, "ffn_down": 3, "gemv": 3, "attn_scores": 4,
            "attn_output": 4, "fp8_square": 5}.get(name, 5)
     ashape = (Z, M, K) if Z > 1 else (M, K)
@@ -139,7 +173,13 @@ def make_inputs(name, copies, dev):
 def launcher(name, sets, dbias, sa, sb):
     import tiled_matrix_multiplication_amd as tmm
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
-    if name == "gemv":
+    if name in ATTENTION:
+        scale = float(K) ** -0.5
+
+        def run(i):
+            Q, Kt, V, O = sets[i % len(sets)]
+            tmm.tmm_attention_fwd(Q, Kt, V, O, scale=scale)
+    elif name == "gemv":
         def run(i):
             W, x, y = sets[i % len(sets)]
             tmm.tmm_gemv(W, x.view(-1)[:K], y.view(-1), bias=dbias)
@@ -229,7 +269,7 @@ def time_graph(run, launches, replays, warmup):
 def copies_for(name):
     """Enough distinct input copies that a launch finds its operands out of the MALL."""
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
-    per = Z * ((M * K + K * N) * BYTES[fin] + M * N * BYTES[fout])
+    per = work(name)[1] if name in ATTENTION else Z * ((M * K + K * N) * BYTES[fin] + M * N * BYTES[fout])
     return int(max(1, min(20, np.ceil(600e6 / per))))
 
 
@@ -253,8 +293,7 @@ def measure(name, steps, warmup, dev):
         sa, sb = host[3], host[4]
     run = launcher(name, sets, dbias, sa, sb)
     ms, wall = time_steps(run, steps, warmup)
-    flops = gemm_flops(M, N, K, Z)
-    nbytes = gemm_bytes(M, N, K, BYTES[fin], BYTES[fout], Z, bias)
+    flops, nbytes = work(name)
     out = {"ms": ms, "wall": wall, "flops": flops, "bytes": nbytes, "copies": copies,
            "sets": sets, "host": host}
     if name == "gemv":
@@ -323,6 +362,8 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
     what the same counters read for a plain copy of `copy_bytes` bytes."""
     if name == "gemv":
         kernel_substr = "gemv"
+    elif name in ATTENTION:
+        kernel_substr = "attn_fwd"
     f_k, nf = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", kernel_substr)
     w_k, nw = _counter_per_dispatch(write_csv, "WRITE_SIZE", kernel_substr)
     f_c, _ = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", copy_substr)
@@ -335,7 +376,7 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
            "fetch_bytes": f_k * fetch_scale, "write_bytes": w_k * write_scale,
            "bytes_per_launch": f_k * fetch_scale + w_k * write_scale}
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
-    out["algorithmic_bytes"] = gemm_bytes(M, N, K, BYTES[fin], BYTES[fout], Z, bias)
+    out["algorithmic_bytes"] = work(name)[1]
     os.makedirs(PROFILES, exist_ok=True)
     json.dump(out, open(traffic_path(name), "w"), indent=1)
     print(json.dumps(out))
@@ -370,6 +411,8 @@ def cpu_baseline(name, r, target_s=20.0):
     Times it on the host cores (OpenMP threads), scales to the metric's unit,
     and compares the sampled GPU rows against it."""
     import oracle
+    if name in ATTENTION:
+        return cpu_baseline_attention(name, r, target_s)
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
     A, B, bvec, sa, sb = r["host"]
     if Z > 1:
@@ -404,6 +447,34 @@ def cpu_baseline(name, r, target_s=20.0):
                       f" of the {describe(name)} product ({len(idx)}x{N}x{K}, fp64 triple loop; "
                       f"time includes decoding the inputs)",
             "sample_rel_fro_vs_gpu": err}
+
+
+def cpu_baseline_attention(name, r, target_s=20.0):
+    """The oracle's attention on whole heads (every query, key and value of
+    heads 0, 1, ...): one head is timed first, then as many heads as fill
+    about target_s seconds; scaled to TFLOP/s like the GPU figure."""
+    import oracle
+    Nq, Nk, D, Z, fin, fout, tb, bias = WORKLOADS[name]
+    Q, Kt, V, _, _ = r["host"]
+    scale = float(D) ** -0.5
+
+    def run_heads(n):
+        t0 = time.perf_counter()
+        outs = [oracle.attention(fin, Q[z], Kt[z], V[z], scale) for z in range(n)]
+        return outs, time.perf_counter() - t0
+
+    outs, t1 = run_heads(1)
+    n = int(min(Z, max(1, target_s // max(t1, 1e-3))))
+    t = t1
+    if n > 1:
+        outs, t = run_heads(n)
+    O = r["sets"][0][3]
+    errs = [compare_rows(O[z], np.arange(Nq), outs[z]) for z in range(n)]
+    return {"value": round(attention_flops(Nq, Nk, D, n) / t / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.threads(), "kind": "oracle", "seconds": round(t, 2),
+            "sample": (f"{n} of {Z} heads of the {describe(name)} workload, every query, key and "
+                       f"value of each (fp64, max-subtracted softmax; time includes decoding)"),
+            "sample_rel_fro_vs_gpu": max(errs)}
 
 
 def main(argv=None):
@@ -445,8 +516,9 @@ def main(argv=None):
     r = measure(name, args.steps, args.warmup, dev)
     roof = roofline_entry(name, r)
     value = r["flops"] / (r["ms"] * 1e-3) / 1e12
+    per = "4 Nq Nk D batch / t" if name in ATTENTION else "2MNK/t"
     line = {
-        "metric": METRIC if name == "square_bf16" else f"{describe(name)}: TFLOP/s (2MNK/t)",
+        "metric": METRIC if name == "square_bf16" else f"{describe(name)}: TFLOP/s ({per})",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -463,6 +535,9 @@ def main(argv=None):
                    "input_copies_rotated": r["copies"]},
         "roofline": roof,
     }
+    if name in ATTENTION:
+        line["config"] = {"workload": describe(name), "Nq": M, "Nk": N, "D": K, "batch_heads": Z,
+                          "out": fout, "scale": "1/sqrt(D)", "input_copies_rotated": r["copies"]}
     if name == "square_bf16" and not args.no_gemv:
         g = measure("gemv", max(1000, args.steps), max(20, args.warmup), dev)
         gbs = g["bytes"] / (g["ms"] * 1e-3) / 1e9

@@ -150,7 +150,8 @@ int tmm_gemv(int64_t N, int64_t K, tmm_dtype w_type, tmm_dtype y_type,
  *   rounded to in_type.
  *   D must be 64 or 128 (TMM_ERR_DIM otherwise); Nk >= 1 when Nq > 0
  *   (TMM_ERR_DIM); every pointer 16-byte aligned and every ld and stride a
- *   multiple of 8 elements (TMM_ERR_ALIGN); scale finite (TMM_ERR_SCALE).
+ *   multiple of 8 elements (TMM_ERR_ALIGN); ldk, ldv <= 2^24 (TMM_ERR_LD);
+ *   scale finite, also times log2(e) (TMM_ERR_SCALE).
  * Quick return: batch == 0 or Nq == 0.
  */
 int tmm_attention_fwd(int64_t batch, int64_t Nq, int64_t Nk, int64_t D,

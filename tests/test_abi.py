@@ -153,6 +153,9 @@ def test_attention_validation(tmm):
     assert attn(tmm, ld=64) == -2                     # ld below D
     assert attn(tmm, so=64 * 128 - 1) == -6           # O matrices overlap
     assert attn(tmm, scale=float("inf")) == -5
+    assert attn(tmm, scale=3e38) == -5                # finite, but not once times log2(e)
+    assert tmm.lib.tmm_attention_fwd(1, 64, 64, 128, 2, 2, FAKE, 128, 0, FAKE2, (1 << 24) + 8, 0,
+                                     FAKE3, 128, 0, FAKE, 128, 0, 0.1, None) == -2
     assert attn(tmm, Q=None) == -3
     assert attn(tmm, ld=132, sq=64 * 132) == -7       # ld not a multiple of 8
     assert attn(tmm, Q=ctypes.c_void_p(0x100008)) == -7   # not 16-byte aligned

@@ -31,6 +31,8 @@
 //     keys past Nk score -inf; the last step divides by l and stores.
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tmm_internal.h"
 
 namespace tmm {
@@ -49,11 +51,13 @@ constexpr int kQw = 32;             // queries per wave
 constexpr int kBQ = kWaves * kQw;   // queries per workgroup
 constexpr int kBK = 64;             // keys per block (step)
 
-// 16-byte direct global->LDS load: lane L's 16 bytes land at LDS byte
+// 16-byte direct global->LDS load of base + off (off: this lane's 32-bit
+// byte offset, base: wave-uniform); lane L's 16 bytes land at LDS byte
 // address m0 + 16 L.  From assembly, so the compiler does not track it; the
 // kernel waits for these loads itself before each barrier and at exit.
-__device__ __forceinline__ void dma16(const char *g, uint32_t m0) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(m0) : "memory");
+__device__ __forceinline__ void dma16(const char *base, uint32_t off, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(m0)
+               : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const char *p) {
@@ -75,19 +79,16 @@ __device__ __forceinline__ int64_t remap_xcd(int64_t pid, int64_t n) {
   return (pid & 7) * per + (pid >> 3);
 }
 
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ uint16_t to_f16(float f) {
-  return __builtin_bit_cast(uint16_t, (_Float16)f);
-}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to two 16-bit values of format F, nearest-even (one packed
+// conversion instruction on gfx950), lo in the low half.
 template <int F>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  if constexpr (F == kBF16) return to_bf16(lo) | ((uint32_t)to_bf16(hi) << 16);
-  else return to_f16(lo) | ((uint32_t)to_f16(hi) << 16);
+  if constexpr (F == kBF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
 }
 
 // LDS swizzles.  K tile: the score fragments read 32 consecutive rows at one
@@ -133,28 +134,54 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_fwd_kernel(AttnParams p) 
 
   // Q fragments (second operand of S^T = K Q^T), slice c: lane (query
   // q0 + l32, g) holds Q[q][16 c + 8 g .. +7].  Rows past Nq repeat the last
-  // query; their outputs are not stored.
+  // query; their outputs are not stored.  A negative scale is moved onto Q
+  // (flipping sign bits is exact), so the kernel's scale c is >= 0 and the
+  // largest scaled score is c times the largest raw score.
+  const bool neg = p.scale_log2 < 0.f;
+  const float c2 = neg ? -p.scale_log2 : p.scale_log2;   // log2(e) * |scale|
   i32x4 qf[DS];
   {
     const int64_t qrow = min64(q0 + l32, Nq - 1);
+    const int flip = neg ? (int)0x80008000u : 0;
 #pragma unroll
-    for (int c = 0; c < DS; ++c) qf[c] = *(const i32x4 *)(Qz + (qrow * p.ldq + 16 * c + 8 * g) * E);
+    for (int c = 0; c < DS; ++c) {
+      qf[c] = *(const i32x4 *)(Qz + (qrow * p.ldq + 16 * c + 8 * g) * E);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) qf[c][w] ^= flip;
+    }
   }
 
   // Direct loads of key block kb into stage st: instruction i of wave w
   // fills rows (w LPT + i) RPI .. +RPI-1 of the K and of the V tile; lane L
-  // lands at row + L/CPR, position L%CPR.  Rows past Nk repeat the last key
-  // (their scores are masked).
+  // lands at row + L/CPR, position L%CPR.  Byte offsets within a block are
+  // 32-bit per lane (rows < 64, ld <= 2^24 elements); the block's base
+  // address is wave-uniform.  In the last, partial block rows past Nk repeat
+  // the last key (their weights are set to 0).
   const uint32_t lds0 = lds_addr(lds);
+  const int pos = lane % CPR;
+  uint32_t koff[LPT], voff[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int row = (wave * LPT + i) * RPI + lane / CPR;
+    koff[i] = (uint32_t)(row * p.ldk * E) + ((pos ^ kswz<CPR>(row)) << 4);
+    voff[i] = (uint32_t)(row * p.ldv * E) + ((pos ^ vswz(row)) << 4);
+  }
   auto issue = [&](int64_t kb, int st) __attribute__((always_inline)) {
+    const char *kbase = Kz + kb * kBK * p.ldk * E;
+    const char *vbase = Vz + kb * kBK * p.ldv * E;
+    const int64_t left = Nk - kb * kBK;   // keys of this block below Nk
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int row = (wave * LPT + i) * RPI + lane / CPR;
-      const int64_t key = min64(kb * kBK + row, Nk - 1);
-      const int pos = lane % CPR;
       const uint32_t dst = lds0 + st * STAGE + (wave * LPT + i) * RPI * RB;
-      dma16(Kz + key * p.ldk * E + ((pos ^ kswz<CPR>(row)) << 4), dst);
-      dma16(Vz + key * p.ldv * E + ((pos ^ vswz(row)) << 4), dst + TILE);
+      uint32_t ko = koff[i], vo = voff[i];
+      if (left < kBK) {
+        const int row = (wave * LPT + i) * RPI + lane / CPR;
+        const int64_t r = row < left ? row : left - 1;
+        ko = (uint32_t)(r * p.ldk * E) + ((pos ^ kswz<CPR>(row)) << 4);
+        vo = (uint32_t)(r * p.ldv * E) + ((pos ^ vswz(row)) << 4);
+      }
+      dma16(kbase, ko, dst);
+      dma16(vbase, vo, dst + TILE);
     }
   };
 
@@ -163,14 +190,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_fwd_kernel(AttnParams p) 
   for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[b][r] = 0.f;
+  // Running maximum m (of c * score, base-2 units) and exp-sum l of this
+  // lane's query.  m is raised only when a block's maximum exceeds it by
+  // more than kLazy, so weights 2^(c s - m) stay below 2^kLazy and the
+  // rescaling of O and l is skipped for most blocks; O / l is the same for
+  // any m at or below the true maximum.
+  constexpr float kLazy = 8.f;
   float m_run = -__builtin_inff(), l_run = 0.f;
 
   const int64_t nblk = (Nk + kBK - 1) / kBK;
+  const int64_t nfull = Nk / kBK;
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) lgkmcnt(0)
   __syncthreads();
 
-  for (int64_t kb = 0; kb < nblk; ++kb) {
+  auto block = [&](int64_t kb, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     const int st = (int)(kb & 1);
     if (kb + 1 < nblk) issue(kb + 1, st ^ 1);
     const char *Kt = lds + st * STAGE;
@@ -197,36 +232,41 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_fwd_kernel(AttnParams p) 
 
     // ---- online softmax of this lane's query.  Register r of half h2
     // holds key 32 h2 + 8 (r / 4) + 4 g + r % 4 of the block.
+    const int left = kMasked ? (int)(Nk - kb * kBK) : kBK;
     float mloc = -__builtin_inff();
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t key = kb * kBK + 32 * h2 + 8 * (r >> 2) + 4 * g + (r & 3);
-        float s = acc_s[h2][r] * p.scale_log2;
-        if (key >= Nk) s = -__builtin_inff();
-        acc_s[h2][r] = s;
-        mloc = __builtin_fmaxf(mloc, s);
+        if (kMasked && 32 * h2 + 8 * (r >> 2) + 4 * g + (r & 3) >= left) acc_s[h2][r] = -__builtin_inff();
+        mloc = __builtin_fmaxf(mloc, acc_s[h2][r]);
       }
     mloc = __builtin_fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = __builtin_fmaxf(m_run, mloc);   // finite: each block has a key < Nk
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float mcand = mloc * c2;   // finite: each block has a key below Nk
+    const bool raise = mcand > m_run + kLazy;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float m_new = raise ? mcand : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[b][r] *= alpha;
+    }
+    const float nm = -m_run;
     float lsum = 0.f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(acc_s[h2][r] - m_new);
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[h2][r], c2, nm));
+        if (kMasked && 32 * h2 + 8 * (r >> 2) + 4 * g + (r & 3) >= left) e = 0.f;
         acc_s[h2][r] = e;
         lsum += e;
       }
     lsum += __shfl_xor(lsum, 32, 64);
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[b][r] *= alpha;
+    l_run += lsum;
 
     // ---- O^T += V^T P^T, 16 keys per instruction.  Key chunk (h2, h):
     // positions 0-3 of a lane are keys base + 4 g + 0..3 and positions 4-7
@@ -264,7 +304,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_fwd_kernel(AttnParams p) 
 
     __builtin_amdgcn_s_waitcnt(0);   // next block's loads and this block's reads done
     __syncthreads();
-  }
+  };
+
+  for (int64_t kb = 0; kb < nfull; ++kb) block(kb, std::false_type{});
+  if (nfull < nblk) block(nfull, std::true_type{});
 
   // ---- O = O^T / l: lane (query q0 + l32, g), block b, register r holds
   // column 32 b + 8 (r / 4) + 4 g + r % 4; four consecutive columns per store.

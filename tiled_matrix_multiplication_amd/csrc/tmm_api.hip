@@ -234,6 +234,9 @@ int tmm_gemv(int64_t N, int64_t K, tmm_dtype w_type, tmm_dtype y_type, const voi
   return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
 }
 
+// Largest K / V leading dimension of the attention kernel (elements).
+constexpr int64_t kMaxAttnLd = (int64_t)1 << 24;
+
 int tmm_attention_fwd(int64_t batch, int64_t Nq, int64_t Nk, int64_t D, tmm_dtype in_type,
                       tmm_dtype out_type, const void *Q, int64_t ldq, int64_t strideQ,
                       const void *K, int64_t ldk, int64_t strideK, const void *V, int64_t ldv,
@@ -244,9 +247,11 @@ int tmm_attention_fwd(int64_t batch, int64_t Nq, int64_t Nk, int64_t D, tmm_dtyp
       (out_type != in_type && out_type != TMM_F32))
     return TMM_ERR_DTYPE;
   if (ldq < D || ldk < D || ldv < D || ldo < D) return TMM_ERR_LD;
+  if (ldk > kMaxAttnLd || ldv > kMaxAttnLd) return TMM_ERR_LD;  // 32-bit offsets within a key block
   if (strideQ < 0 || strideK < 0 || strideV < 0 || strideO < 0) return TMM_ERR_STRIDE;
   if (batch > 1 && Nq > 0 && strideO < (Nq - 1) * ldo + D) return TMM_ERR_STRIDE;
-  if (!isfinite(scale)) return TMM_ERR_SCALE;
+  const float scale_log2 = scale * 1.4426950408889634f;   // exponentials are base 2
+  if (!isfinite(scale) || !isfinite(scale_log2)) return TMM_ERR_SCALE;
   if (batch == 0 || Nq == 0) return TMM_OK;
   if (Nk == 0) return TMM_ERR_DIM;  // softmax over no keys
   if (!Q || !K || !V || !O) return TMM_ERR_NULL;
@@ -261,7 +266,7 @@ int tmm_attention_fwd(int64_t batch, int64_t Nq, int64_t Nk, int64_t D, tmm_dtyp
   p.K = K; p.ldk = ldk; p.strideK = strideK;
   p.V = V; p.ldv = ldv; p.strideV = strideV;
   p.O = O; p.ldo = ldo; p.strideO = strideO;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  p.scale_log2 = scale_log2;
   const hipError_t err = tmm::launch_attention((Fmt)in_type, (Fmt)out_type, (int)D, p, stream);
   return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
 }
