@@ -88,6 +88,12 @@ WORKLOADS = {
     "ragged_4097x511x1023": (4097, 511, 1023, 1, "bf16", "bf16", False, False),
     "f32_256": (256, 256, 256, 1, "f32", "f32", False, False),
     "gemv": (1, 4096, 4096, 1, "bf16", "bf16", True, True),
+    # skinny M: batched decode through one 4096 x 4096 linear layer (the GEMM
+    # page's batch-size table), fp16 as there, + bias
+    "skinny_m4": (4, 4096, 4096, 1, "f16", "f16", True, True),
+    "skinny_m16": (16, 4096, 4096, 1, "f16", "f16", True, True),
+    "skinny_m64": (64, 4096, 4096, 1, "f16", "f16", True, True),
+    "skinny_m256": (256, 4096, 4096, 1, "f16", "f16", True, True),
     # fused attention: (Nq queries, Nk keys, D head size, batch x heads, in, out, -, -)
     "attn_fused": (2048, 2048, 128, 128, "f16", "f16", True, False),
 }
@@ -141,7 +147,7 @@ def make_inputs(name, copies, dev):
                 for _ in range(copies)]
         return sets, None, (Q, Kt, V, 1.0, 1.0)
     cfg = {"square_bf16": 2, "qkv": 3, "ffn_up": 3, "ffn_down": 3, "gemv": 3, "attn_scores": 4,
-           "attn_output": 4, "fp8_square": 5}.get(name, 5)
+           "attn_output": 4, "fp8_square": 5}.get(name, 7 if name.startswith("skinny") else 5)
     ashape = (Z, M, K) if Z > 1 else (M, K)
     bshape = ((Z, N, K) if tb else (Z, K, N)) if Z > 1 else ((N, K) if tb else (K, N))
     sa = sb = 1.0
@@ -296,7 +302,7 @@ def measure(name, steps, warmup, dev):
     flops, nbytes = work(name)
     out = {"ms": ms, "wall": wall, "flops": flops, "bytes": nbytes, "copies": copies,
            "sets": sets, "host": host}
-    if name == "gemv":
+    if name == "gemv" or name.startswith("skinny"):
         # the eager call is host-bound at this size: time the kernel in a graph
         out["ms_eager"] = ms
         out["ms"] = time_graph(run, 100, max(1, steps // 100), warmup)
@@ -324,13 +330,33 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "tiled_matrix_multiplication_amd", "csrc")
 
 
-def kernel_source_hash():
-    """Hash of the HIP sources: counter-derived traffic is only reported for
-    the kernel build it was measured on."""
+# Sources that define each workload's dominant kernel (the host dispatch and
+# the shared parameter header are not part of it).
+KERNEL_SOURCES = {
+    "gemm": ["gemm_mfma.h", "gemm_ring.h", "gemm_f32.hip", "gemm_bf16.hip", "gemm_f16.hip", "gemm_f8.hip"],
+    "gemv": ["gemv.hip"],
+    "skinny": ["gemm_skinny.hip"],
+    "attention": ["attention.hip"],
+}
+
+
+def kernel_family(name):
+    if name == "gemv":
+        return "gemv"
+    if name in ATTENTION:
+        return "attention"
+    if name.startswith("skinny"):
+        return "skinny"
+    return "gemm"
+
+
+def kernel_source_hash(name):
+    """Hash of the sources of the workload's kernel: counter-derived traffic
+    is only reported for the kernel code it was measured on."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(CSRC, "*.hip"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+    for f in KERNEL_SOURCES[kernel_family(name)]:
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -345,7 +371,7 @@ def traffic_from_profile(name):
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    return d["bytes_per_launch"] if d.get("source_hash") == kernel_source_hash() else None
+    return d["bytes_per_launch"] if d.get("source_hash") == kernel_source_hash(name) else None
 
 
 def _counter_per_dispatch(csv_path, counter, kernel_substr):
@@ -364,13 +390,16 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
         kernel_substr = "gemv"
     elif name in ATTENTION:
         kernel_substr = "attn_fwd"
+    elif name.startswith("skinny"):
+        kernel_substr = "gemm_skinny"
     f_k, nf = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", kernel_substr)
     w_k, nw = _counter_per_dispatch(write_csv, "WRITE_SIZE", kernel_substr)
     f_c, _ = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", copy_substr)
     w_c, _ = _counter_per_dispatch(copy_write_csv, "WRITE_SIZE", copy_substr)
     fetch_scale = copy_bytes / f_c     # bytes per counter unit, from the copy's reads
     write_scale = copy_bytes / w_c
-    out = {"workload": describe(name), "source_hash": kernel_source_hash(),
+    out = {"workload": describe(name), "source_hash": kernel_source_hash(name),
+           "hash_covers": KERNEL_SOURCES[kernel_family(name)],
            "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k, "dispatches": [nf, nw],
            "copy_bytes": copy_bytes, "copy_fetch_kib": f_c, "copy_write_kib": w_c,
            "fetch_bytes": f_k * fetch_scale, "write_bytes": w_k * write_scale,

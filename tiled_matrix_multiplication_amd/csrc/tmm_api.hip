@@ -4,6 +4,7 @@
 //
 // Every check runs on the host before any HIP call, so a rejected call has
 // no side effect and the checks are testable on a machine without a GPU.
+#include <stdio.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -89,9 +90,10 @@ int cu_count() {
 }
 
 // TMM_FORCE_TILE = "256x256" | "256x128" | "128x128" | "256x256w4" | "256x256s2" |
-// "256x256r" pins the tile shape for measurements and tile-by-tile tests
-// ("256x256s2": 256x256 tiles on the two-stage kernel only; "256x256r": on
-// the ring kernel wherever it applies, K-contiguous B included).
+// "256x256r" | "skinny" pins the tile shape for measurements and tile-by-tile
+// tests ("256x256s2": 256x256 tiles on the two-stage kernel only; "256x256r":
+// on the ring kernel wherever it applies, K-contiguous B included; "skinny":
+// the skinny-M kernel wherever it applies, any M).
 // Read on every call so that a test can switch it; anything else leaves the
 // choice to pick_tile.
 int forced_tile() {
@@ -103,7 +105,51 @@ int forced_tile() {
   if (!strcmp(s, "256x256w4")) return tmm::kTile256x256w4;
   if (!strcmp(s, "256x256s2")) return tmm::kTile256x256s2;
   if (!strcmp(s, "256x256r")) return tmm::kTile256x256r;
+  if (!strcmp(s, "skinny")) return tmm::kTileSkinny;
   return -1;
+}
+
+// Largest M for which the skinny-M kernel is chosen automatically.
+constexpr int64_t kSkinnyMaxM = 256;
+
+// Skinny tile (bm, bn in 16 / 32 / 64): the least operand traffic into the
+// CUs -- every tile reads its bm rows of A and its bn rows of B over all of
+// K, i.e. K (M ceil(N/bn) + N ceil(M/bm)) elements -- among the shapes that
+// give every CU a tile (the most tiles if none does).
+void pick_skinny(int64_t M, int64_t N, int64_t batch, int *bm, int *bn) {
+  // TMM_SKINNY_TILE = "<bm>x<bn>" (each 16, 32 or 64) pins the tile for
+  // measurements.
+  if (const char *e = getenv("TMM_SKINNY_TILE")) {
+    int m = 0, n = 0;
+    if (sscanf(e, "%dx%d", &m, &n) == 2 && (m == 16 || m == 32 || m == 64) &&
+        (n == 16 || n == 32 || n == 64)) {
+      *bm = m;
+      *bn = n;
+      return;
+    }
+  }
+  const int64_t cus = cu_count();
+  double best = 1e300;
+  int64_t best_tiles = -1;
+  bool best_full = false;
+  for (int m : {16, 32, 64}) {
+    for (int n : {16, 32, 64}) {
+      const int64_t tm = (M + m - 1) / m, tn = (N + n - 1) / n;
+      const int64_t tiles = tm * tn * batch;
+      const double traffic = (double)M * tn + (double)N * tm;
+      const bool full = tiles >= cus;
+      const bool better = full ? (!best_full || traffic < best)
+                               : (!best_full && (tiles > best_tiles ||
+                                                 (tiles == best_tiles && traffic < best)));
+      if (better) {
+        best = traffic;
+        best_tiles = tiles;
+        best_full = full;
+        *bm = m;
+        *bn = n;
+      }
+    }
+  }
 }
 
 // Tile shape with the least estimated time: rounds of `cus` concurrent
@@ -111,7 +157,7 @@ int forced_tile() {
 // efficiency (bigger tiles reuse each loaded byte more).
 tmm::Tile pick_tile(int64_t M, int64_t N, int64_t batch, int ab) {
   const int f = forced_tile();
-  if (f >= 0) return (tmm::Tile)f;
+  if (f >= 0 && f != tmm::kTileSkinny) return (tmm::Tile)f;
   if (ab == TMM_F32) return tmm::kTile128x128;
   const int cus = cu_count();
   const double eff[tmm::kNumAutoTiles] = {1.0, 0.85, 0.65};
@@ -161,7 +207,8 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
   hipError_t err;
   if (K == 0) {
     err = tmm::launch_fill((Fmt)c, p, stream);
-  } else if (M == 1 && batch == 1 && trans_b && ab != TMM_F8E4M3) {
+  } else if (M == 1 && batch == 1 && trans_b && ab != TMM_F8E4M3 &&
+             forced_tile() != tmm::kTileSkinny) {
     // y = W . x with W = B (N x K): the memory-bound matrix-vector path.
     tmm::GemvParams g;
     g.N = N; g.K = K; g.W = B; g.ldw = ldb; g.x = A; g.y = C; g.bias = bias;
@@ -178,8 +225,18 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
                      (ldb * e) % 16 == 0 &&
                      (batch == 1 || ((sA * e) % 16 == 0 && (sB * e) % 16 == 0)) &&
                      (trans_b || (N * e) % 16 == 0);
-    const tmm::Tile tile = vec ? pick_tile(M, N, batch, ab) : tmm::kTile128x128;
-    err = dispatch_gemm(ab, c, trans_b != 0, tile, vec, p, stream);
+    const int f = forced_tile();
+    const bool skinny_ok = vec && trans_b && (ab == TMM_BF16 || ab == TMM_F16);
+    if (skinny_ok && (f == tmm::kTileSkinny || (f < 0 && M <= kSkinnyMaxM))) {
+      int bm, bn;
+      pick_skinny(M, N, batch, &bm, &bn);
+      const int ce = elem_bytes(c);
+      const bool vec_c = aligned(C, 4 * ce) && ldc % 4 == 0 && (batch == 1 || sC % 4 == 0);
+      err = tmm::launch_gemm_skinny((Fmt)ab, (Fmt)c, bm, bn, vec_c, p, stream);
+    } else {
+      const tmm::Tile tile = vec ? pick_tile(M, N, batch, ab) : tmm::kTile128x128;
+      err = dispatch_gemm(ab, c, trans_b != 0, tile, vec, p, stream);
+    }
   }
   return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
 }

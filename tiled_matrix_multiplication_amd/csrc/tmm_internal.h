@@ -20,6 +20,7 @@ enum Tile : int {
   kTile256x256w4 = 3,
   kTile256x256s2 = 4,  // 256x256 on the two-stage kernel only
   kTile256x256r = 5,   // 256x256 on the ring kernel wherever it applies (also trans_b)
+  kTileSkinny = 6,     // the skinny-M kernel (16-bit NT only); chosen in the dispatch
   kNumAutoTiles = 3
 };
 
@@ -56,6 +57,12 @@ hipError_t launch_gemm_f16(Fmt c, bool trans_b, Tile tile, bool vec, const GemmP
                            hipStream_t stream);
 hipError_t launch_gemm_f8(Fmt c, bool trans_b, Tile tile, bool vec, const GemmParams &p,
                           hipStream_t stream);
+
+// Skinny-M GEMM (16-bit inputs, B stored N x K, every row of A and B
+// 16-byte aligned): bm x bn workgroup tiles, bm, bn in {16, 32, 64};
+// vec_c allows 4-column vector stores (C aligned for them).
+hipError_t launch_gemm_skinny(Fmt ab, Fmt c, int bm, int bn, bool vec_c, const GemmParams &p,
+                              hipStream_t stream);
 
 // C = bias broadcast (or 0) for the K == 0 empty sum.
 hipError_t launch_fill(Fmt c, const GemmParams &p, hipStream_t stream);
