@@ -60,11 +60,13 @@ def _load():
     lib.oracle_round.argtypes = [ctypes.c_int, vp, vp, i64]
     lib.oracle_gemm.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, vp, i64,
                                 ctypes.c_int, vp, dp, dp, vp, i64, vp]
+    lib.oracle_gemm_ex.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64,
+                                   vp, i64, dp, dp, vp, vp, ctypes.c_int, vp, i64, vp]
     lib.oracle_threads.argtypes = []
     lib.oracle_attention.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, vp, i64, vp, i64,
                                      ctypes.c_double, vp, i64, vp]
     for f in (lib.oracle_decode, lib.oracle_round, lib.oracle_gemm, lib.oracle_threads,
-              lib.oracle_attention):
+              lib.oracle_attention, lib.oracle_gemm_ex):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -139,6 +141,46 @@ def gemm(fmt, A: np.ndarray, B: np.ndarray, trans_b: bool = False,
                              max(N, 1), _ptr(T))
     if rc:
         raise ValueError(f"oracle_gemm failed ({rc})")
+    return (C, T) if want_abs else C
+
+
+def gemm_ex(fmt, A: np.ndarray, B: np.ndarray, trans_a: bool = False, trans_b: bool = False,
+            alpha: float = 1.0, beta: float = 0.0, C_in: np.ndarray | None = None,
+            bias: np.ndarray | None = None, relu: bool = False, want_abs: bool = False):
+    """o = act(alpha * op(A) . op(B) + bias + beta * C_in) in float64.
+
+    A: (M, K) bit patterns, or (K, M) when ``trans_a``; B: (K, N), or (N, K)
+    when ``trans_b``; C_in: (M, N) values (float64; ignored when None);
+    act = max(0, .) when ``relu``.  Returns o, and with ``want_abs`` also
+    T = |alpha| sum_k |a'_ik b'_kj| + |bias_j| + |beta c_ij|.
+    """
+    f = _fmt(fmt)
+    A = _rowmajor(np.asarray(A))
+    B = _rowmajor(np.asarray(B))
+    if A.dtype != _BITS[f] or B.dtype != _BITS[f] or A.ndim != 2 or B.ndim != 2:
+        raise TypeError("A and B must be 2-D arrays of the format's bit patterns")
+    M, K = (A.shape[1], A.shape[0]) if trans_a else A.shape
+    N, K2 = B.shape if trans_b else (B.shape[1], B.shape[0])
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    lda = A.strides[0] // A.itemsize if A.shape[0] > 1 else max(A.shape[1], 1)
+    ldb = B.strides[0] // B.itemsize if B.shape[0] > 1 else max(B.shape[1], 1)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.shape != (N,):
+            raise ValueError("bias must have N entries")
+    cin = None
+    if C_in is not None:
+        cin = np.ascontiguousarray(C_in, dtype=np.float64)
+        if cin.shape != (M, N):
+            raise ValueError("C_in must be M x N")
+    C = np.empty((M, N), dtype=np.float64)
+    T = np.empty((M, N), dtype=np.float64) if want_abs else None
+    rc = _load().oracle_gemm_ex(M, N, K, f, int(bool(trans_a)), int(bool(trans_b)), _ptr(A), lda,
+                                _ptr(B), ldb, float(alpha), float(beta), _ptr(cin), _ptr(bias),
+                                1 if relu else 0, _ptr(C), max(N, 1), _ptr(T))
+    if rc:
+        raise ValueError(f"oracle_gemm_ex failed ({rc})")
     return (C, T) if want_abs else C
 
 

@@ -34,6 +34,8 @@
  * value, ties to the even significand", written from that definition on the
  * format's grid of representable values.
  *
+ * oracle_gemm_ex states the full BLAS form the same way (see there).
+ *
  * oracle_attention states softmax(scale Q K^T) V the same way (see there).
  *
  * Each pin of this file lives in tests/test_oracle.py.
@@ -268,6 +270,79 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K, int fmt, const void *A,
   }
   free(bp);
   return fail ? -3 : 0;
+}
+
+/*
+ * The full BLAS form of the product with a fused activation:
+ *
+ *   o[i][j] = act( alpha * sum_{k<K} a'[i][k] * b'[k][j] + bias[j] + beta * c[i][j] )
+ *
+ *   - C = alpha * op(A) * op(B) + beta * C with op = identity or transpose
+ *     per operand: "GEMM to FlashAttention" page, the BLAS level-3 line and
+ *     the "GEMM interface" box (transa / transb, alpha, beta);
+ *   - bias per output feature added to the product, then the activation
+ *     f(x) = max(0, x) (ReLU): CMU 15-418 Lecture 27 notes section 2.1 (a
+ *     unit computes f(sum_i x_i w_i + b), ReLU one such f) and the fused
+ *     scale / bias / ReLU epilogue of its conv_fused listing (section 3.1).
+ *     The order bias-then-beta is immaterial in exact arithmetic; the
+ *     activation comes last.
+ *
+ *   A  : trans_a ? K x M : M x K inputs at stride lda  (a' = op(A), M x K)
+ *   B  : trans_b ? N x K : K x N inputs at stride ldb  (b' = op(B), K x N)
+ *   Cin: NULL (beta ignored) or M x N doubles at stride ldc, the old C
+ *   C  : M x N doubles at stride ldc (written; may be the same array as Cin)
+ *   T  : NULL or like C: |alpha| sum_k |a' b'| + |bias| + |beta c|, the
+ *        scale of the error of any fp32 evaluation
+ *   act: 0 none, 1 ReLU
+ */
+int oracle_gemm_ex(int64_t M, int64_t N, int64_t K, int fmt, int trans_a, int trans_b,
+                   const void *A, int64_t lda, const void *B, int64_t ldb, double alpha,
+                   double beta, const double *Cin, const float *bias, int act, double *C,
+                   int64_t ldc, double *T) {
+  if (M < 0 || N < 0 || K < 0 || fmt < ORC_F32 || fmt > ORC_E4M3 || act < 0 || act > 1)
+    return -1;
+  if (lda < (trans_a ? M : K) || ldb < (trans_b ? K : N) || ldc < N)
+    return -2;
+  if (M == 0 || N == 0)
+    return 0;
+  /* a' (M x K) and b' (K x N) as doubles */
+  const int64_t Kd = K > 0 ? K : 1;
+  double *ap = (double *)malloc(sizeof(double) * (size_t)M * (size_t)Kd);
+  double *bp = (double *)malloc(sizeof(double) * (size_t)Kd * (size_t)N);
+  if (!ap || !bp) {
+    free(ap);
+    free(bp);
+    return -3;
+  }
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t k = 0; k < K; ++k)
+      ap[i * Kd + k] = trans_a ? dec_at(fmt, A, k * lda + i) : dec_at(fmt, A, i * lda + k);
+  for (int64_t k = 0; k < K; ++k)
+    for (int64_t j = 0; j < N; ++j)
+      bp[k * N + j] = trans_b ? dec_at(fmt, B, j * ldb + k) : dec_at(fmt, B, k * ldb + j);
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < N; ++j) {
+      double sum = 0.0, sabs = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double t = ap[i * Kd + k] * bp[k * N + j];
+        sum += t;
+        sabs += fabs(t);
+      }
+      const double b = bias ? (double)bias[j] : 0.0;
+      const double c = Cin ? beta * Cin[i * ldc + j] : 0.0;
+      double v = alpha * sum + b + c;
+      if (act == 1 && !(v > 0.0))
+        v = 0.0;
+      if (T)
+        T[i * ldc + j] = fabs(alpha) * sabs + fabs(b) + fabs(c);
+      C[i * ldc + j] = v;
+    }
+  }
+  free(ap);
+  free(bp);
+  return 0;
 }
 
 /*
