@@ -92,8 +92,15 @@ enum tmm_status {
   TMM_ERR_SCALE = -5,  /* scale != 1 for a non-fp8 type, or a non-finite one  */
   TMM_ERR_STRIDE = -6, /* negative batch stride, or C matrices that overlap   */
   TMM_ERR_ALIGN = -7,  /* pointer not aligned to its element size            */
-  TMM_ERR_LAUNCH = -8  /* HIP reported an error at launch                     */
+  TMM_ERR_LAUNCH = -8, /* HIP reported an error at launch                     */
+  TMM_ERR_ARG = -9     /* unknown activation code                            */
 };
+
+/* Activation applied last by tmm_gemm_ex. */
+typedef enum tmm_activation {
+  TMM_ACT_NONE = 0,
+  TMM_ACT_RELU = 1 /* max(0, x) */
+} tmm_activation;
 
 /*
  * C = scale_a*scale_b * A . op(B) (+ bias).  M x N outputs, K-long sums.
@@ -161,6 +168,32 @@ int tmm_attention_fwd(int64_t batch, int64_t Nq, int64_t Nk, int64_t D,
                       const void *V, int64_t ldv, int64_t strideV,
                       void *O, int64_t ldo, int64_t strideO, float scale,
                       hipStream_t stream);
+
+/*
+ * The full BLAS form with a fused activation, batched:
+ *   C[z] = act( alpha * op(A[z]) . op(B[z]) + bias + beta * C[z] )
+ * with op(A) = A (M x K, lda >= K) or A^T (A stored K x M, lda >= M) by
+ * trans_a, op(B) = B (K x N, ldb >= N) or B^T (B stored N x K, ldb >= K) by
+ * trans_b, for z < batch at strides strideA / strideB / strideC (elements).
+ * ("GEMM to FlashAttention" page: the BLAS level-3 gemm and the GEMM
+ * interface box, transa / transb / alpha / beta / lda / ldb / ldc; CMU
+ * 15-418 Lecture 27 notes section 2.1: a unit computes f(sum x w + b) with
+ * f = ReLU, and the fused scale / bias / ReLU epilogue of section 3.1.)
+ *   The sum is fp32; alpha * sum + bias + beta * old C is formed in fp32,
+ *   the activation applied (TMM_ACT_NONE or TMM_ACT_RELU, else TMM_ERR_ARG)
+ *   and the result rounded once (nearest even) to c_type.  beta == 0 does
+ *   not read C (it may hold anything); alpha and beta must be finite
+ *   (TMM_ERR_SCALE).  For fp8 inputs alpha carries the dequantisation
+ *   scales.  Type pairs as for tmm_gemm; trans_a needs bf16 or fp16 inputs
+ *   (TMM_ERR_DTYPE otherwise).  Quick returns as for tmm_gemm; K == 0 gives
+ *   C = act(bias + beta * old C).  Other limits and errors as for
+ *   tmm_gemm_strided_batched.
+ */
+int tmm_gemm_ex(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type, tmm_dtype c_type,
+                int trans_a, int trans_b, const void *A, int64_t lda, int64_t strideA,
+                const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc,
+                int64_t strideC, int64_t batch, const float *bias, float alpha, float beta,
+                int activation, hipStream_t stream);
 
 /* Static English text of a status code (never NULL). */
 const char *tmm_status_string(int status);

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemv", "tmm_attention_fwd",
+        ["tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemm_ex", "tmm_gemv", "tmm_attention_fwd",
          "tmm_status_string", "tmm_version"])
 
 
@@ -165,3 +165,32 @@ def test_attention_quick_returns(tmm):
     """batch == 0 or Nq == 0 enqueue nothing (NULL pointers are then fine)."""
     assert attn(tmm, Z=0, Q=None, K=None, V=None, O=None) == 0
     assert attn(tmm, Nq=0, Q=None, K=None, V=None, O=None) == 0
+
+
+def gex(tmm, M=64, N=64, K=64, ab=1, c=1, ta=0, tb=0, A=FAKE, lda=None, B=FAKE2, ldb=None,
+        C=FAKE3, ldc=None, batch=1, alpha=1.0, beta=0.0, act=0):
+    lda = (M if ta else K) if lda is None else lda
+    ldb = (K if tb else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return tmm.lib.tmm_gemm_ex(M, N, K, ab, c, ta, tb, A, lda, 0, B, ldb, 0, C, ldc, 0, batch, None,
+                               alpha, beta, act, None)
+
+
+def test_gemm_ex_validation(tmm):
+    """The full form's own checks; the fake pointers would fault if a call
+    got past validation."""
+    assert gex(tmm, act=2) == -9                       # unknown activation
+    assert gex(tmm, act=-1) == -9
+    assert gex(tmm, ab=0, c=0, ta=1) == -4             # trans_a needs 16-bit inputs
+    assert gex(tmm, ab=3, c=1, ta=1) == -4
+    assert gex(tmm, alpha=float("inf")) == -5
+    assert gex(tmm, beta=float("nan")) == -5
+    assert gex(tmm, M=100, ta=1, lda=64) == -2         # A stored K x M needs lda >= M
+    assert gex(tmm, ab=1, c=2) == -4                   # bf16 -> f16 is not a pair
+    assert gex(tmm, A=None) == -3
+    assert "activation" in tmm.lib.tmm_status_string(-9).decode()
+
+
+def test_gemm_ex_quick_returns(tmm):
+    assert gex(tmm, M=0, A=None, B=None, C=None) == 0
+    assert gex(tmm, batch=0, A=None, B=None, C=None) == 0

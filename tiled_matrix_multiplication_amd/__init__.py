@@ -24,7 +24,7 @@ STATUS = {
     -5: "TMM_ERR_SCALE", -6: "TMM_ERR_STRIDE", -7: "TMM_ERR_ALIGN", -8: "TMM_ERR_LAUNCH",
 }
 
-EXPORTS = ("tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemv", "tmm_attention_fwd",
+EXPORTS = ("tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemm_ex", "tmm_gemv", "tmm_attention_fwd",
            "tmm_status_string", "tmm_version")
 
 _DTYPE = {torch.float32: TMM_F32, torch.bfloat16: TMM_BF16, torch.float16: TMM_F16,
@@ -47,12 +47,15 @@ def _load() -> ctypes.CDLL:
     lib.tmm_gemm_strided_batched.argtypes = [i64, i64, i64, ci, ci, ci, vp, i64, i64, vp, i64, i64,
                                              vp, i64, i64, i64, vp, cf, cf, vp]
     lib.tmm_gemv.argtypes = [i64, i64, ci, ci, vp, i64, vp, vp, vp, vp]
+    lib.tmm_gemm_ex.argtypes = [i64, i64, i64, ci, ci, ci, ci, vp, i64, i64, vp, i64, i64, vp, i64,
+                                i64, i64, vp, cf, cf, ci, vp]
     lib.tmm_attention_fwd.argtypes = [i64, i64, i64, i64, ci, ci, vp, i64, i64, vp, i64, i64,
                                       vp, i64, i64, vp, i64, i64, cf, vp]
     lib.tmm_status_string.argtypes = [ci]
     lib.tmm_status_string.restype = ctypes.c_char_p
     lib.tmm_version.argtypes = []
-    for f in (lib.tmm_gemm, lib.tmm_gemm_strided_batched, lib.tmm_gemv, lib.tmm_attention_fwd,
+    for f in (lib.tmm_gemm, lib.tmm_gemm_strided_batched, lib.tmm_gemm_ex, lib.tmm_gemv,
+              lib.tmm_attention_fwd,
               lib.tmm_version):
         f.restype = ci
     return lib
@@ -145,6 +148,34 @@ def tmm_gemm_strided_batched(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
         _ptr(B), _ld(B), int(B.stride(0)), _ptr(C), _ld(C), int(C.stride(0)), Z, _ptr(bias),
         float(scale_a), float(scale_b), ctypes.c_void_p(_stream(stream)))
     _check("tmm_gemm_strided_batched", rc)
+    return C
+
+
+def tmm_gemm_ex(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, bias: torch.Tensor | None = None,
+                trans_a: bool = False, trans_b: bool = False, alpha: float = 1.0, beta: float = 0.0,
+                relu: bool = False, stream=None):
+    """C = act(alpha * op(A) . op(B) + bias + beta * C), act = ReLU when ``relu``.
+
+    2-D tensors, or 3-D (batch, rows, cols) for a batch of problems.  A is
+    (M, K), or (K, M) with ``trans_a``; B is (K, N), or (N, K) with ``trans_b``.
+    """
+    _on_gpu(A, B, C, bias)
+    if A.dim() == 2:
+        A, B, C = A.unsqueeze(0), B.unsqueeze(0), C.unsqueeze(0)
+    Z = A.shape[0]
+    M, K = (A.shape[2], A.shape[1]) if trans_a else (A.shape[1], A.shape[2])
+    N, K2 = (B.shape[1], B.shape[2]) if trans_b else (B.shape[2], B.shape[1])
+    if K2 != K or B.shape[0] != Z or tuple(C.shape) != (Z, M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    if B.dtype != A.dtype:
+        raise TypeError("A and B must have the same element type")
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (N,) or bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous float32 vector of N entries")
+    rc = lib.tmm_gemm_ex(
+        M, N, K, _dtype(A), _dtype(C), int(bool(trans_a)), int(bool(trans_b)), _ptr(A), _ld(A),
+        int(A.stride(0)), _ptr(B), _ld(B), int(B.stride(0)), _ptr(C), _ld(C), int(C.stride(0)), Z,
+        _ptr(bias), float(alpha), float(beta), 1 if relu else 0, ctypes.c_void_p(_stream(stream)))
+    _check("tmm_gemm_ex", rc)
     return C
 
 

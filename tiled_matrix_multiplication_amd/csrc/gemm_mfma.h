@@ -50,6 +50,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int F> struct FmtBytes;
 template <> struct FmtBytes<kF32> { static constexpr int value = 4; };
@@ -146,6 +147,13 @@ __device__ __forceinline__ void store_out(char *C, int64_t idx, float v) {
     ((uint16_t *)C)[idx] = f32_to_f16_rne(v);
 }
 
+// Value of a stored 16-bit output element (the old C of the full form).
+template <int CT>
+__device__ __forceinline__ float in_value(uint16_t u) {
+  if constexpr (CT == kBF16) return __uint_as_float((uint32_t)u << 16);
+  else return (float)__builtin_bit_cast(_Float16, u);
+}
+
 // Output bits of v in the output type (fp32, or bf16 / fp16 nearest-even).
 template <int CT>
 __device__ __forceinline__ uint32_t out_bits(float v) {
@@ -231,6 +239,110 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[FM][FN], char
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next band's writes
     __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Full-form epilogue, C = act(alpha * acc + bias + beta * C_old): the
+// same staging through the wave's LDS area, but as fp32 values and in
+// 16-row halves of each 32-row band (so the area is 16 rows of WT * 4 + 32
+// bytes), then back 4 columns per lane: the old C of those 4 columns is
+// read when beta != 0, added, ReLU applied when act == 1, one
+// nearest-even rounding, and the 4 outputs stored.  Vector loads and
+// stores need C and its row pitch aligned to 4 elements.
+template <int CT, int FM, int FN>
+__device__ __forceinline__ void store_tile_ex(const f32x16 (&acc)[FM][FN], char *st, char *C,
+                                              int64_t ldc, int64_t M, int64_t N, int64_t row0,
+                                              int64_t col0, const float *bias, float alpha,
+                                              float beta, int act, int lane) {
+  constexpr int CE = FmtBytes<CT>::value;
+  constexpr int WT = FN * 32;                 // columns of the wave's block
+  constexpr int P = WT * 4 + 32;              // fp32 staging row pitch (bytes)
+  constexpr int QPR = WT / 4;                 // 4-column quads per row
+  constexpr int NRD = 16 * QPR / 64;          // read instructions per 16-row half
+  static_assert(NRD >= 1 && (16 * QPR) % 64 == 0, "epilogue geometry");
+  const int l32 = lane & 31, g = lane >> 5;
+  const bool vec = ((uintptr_t)C % (4 * CE)) == 0 && (ldc % 4) == 0;
+  float bv[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t col = col0 + j * 32 + l32;
+    bv[j] = (bias && col < N) ? bias[col] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (row0 + i * 32 + hh * 16 >= M) break;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int r = 8 * hh; r < 8 * hh + 8; ++r) {
+          const int lr = 8 * ((r >> 2) & 1) + 4 * g + (r & 3);   // row within the half
+          *(float *)(st + lr * P + (j * 32 + l32) * 4) = acc[i][j][r] * alpha + bv[j];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int t = 0; t < NRD; ++t) {
+        const int q = t * 64 + lane;
+        const int lr = q / QPR, qc = q % QPR;
+        f32x4 v = *(const f32x4 *)(st + lr * P + qc * 16);
+        const int64_t grow = row0 + i * 32 + hh * 16 + lr;
+        const int64_t gcol = col0 + (int64_t)qc * 4;
+        if (grow >= M || gcol >= N) continue;
+        char *dst = C + (grow * ldc + gcol) * CE;
+        const bool full = vec && gcol + 4 <= N;
+        if (beta != 0.f) {
+          f32x4 c = {0.f, 0.f, 0.f, 0.f};
+          if (full) {
+            if constexpr (CE == 4) {
+              c = *(const f32x4 *)dst;
+            } else {
+              const uint64_t w = *(const uint64_t *)dst;
+              c = f32x4{in_value<CT>((uint16_t)w), in_value<CT>((uint16_t)(w >> 16)),
+                        in_value<CT>((uint16_t)(w >> 32)), in_value<CT>((uint16_t)(w >> 48))};
+            }
+          } else {
+            if constexpr (CE == 4) {
+              if (gcol + 0 < N) c[0] = ((const float *)dst)[0];
+              if (gcol + 1 < N) c[1] = ((const float *)dst)[1];
+              if (gcol + 2 < N) c[2] = ((const float *)dst)[2];
+              if (gcol + 3 < N) c[3] = ((const float *)dst)[3];
+            } else {
+              if (gcol + 0 < N) c[0] = in_value<CT>(((const uint16_t *)dst)[0]);
+              if (gcol + 1 < N) c[1] = in_value<CT>(((const uint16_t *)dst)[1]);
+              if (gcol + 2 < N) c[2] = in_value<CT>(((const uint16_t *)dst)[2]);
+              if (gcol + 3 < N) c[3] = in_value<CT>(((const uint16_t *)dst)[3]);
+            }
+          }
+          v += beta * c;
+        }
+        if (act == 1) {
+          v[0] = v[0] > 0.f ? v[0] : 0.f;
+          v[1] = v[1] > 0.f ? v[1] : 0.f;
+          v[2] = v[2] > 0.f ? v[2] : 0.f;
+          v[3] = v[3] > 0.f ? v[3] : 0.f;
+        }
+        if (full) {
+          if constexpr (CE == 4) {
+            *(f32x4 *)dst = v;
+          } else {
+            const uint64_t w = (uint64_t)out_bits<CT>(v[0]) | ((uint64_t)out_bits<CT>(v[1]) << 16) |
+                               ((uint64_t)out_bits<CT>(v[2]) << 32) |
+                               ((uint64_t)out_bits<CT>(v[3]) << 48);
+            *(uint64_t *)dst = w;
+          }
+        } else {
+          if (gcol + 0 < N) store_out<CT>(dst, 0, v[0]);
+          if (gcol + 1 < N) store_out<CT>(dst, 1, v[1]);
+          if (gcol + 2 < N) store_out<CT>(dst, 2, v[2]);
+          if (gcol + 3 < N) store_out<CT>(dst, 3, v[3]);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next half's writes
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 
@@ -355,7 +467,10 @@ __device__ __forceinline__ void interleave() {
 
 // ---------------------------------------------------------------- kernel
 
-template <int AB, int CT, bool NT, int BM, int BN, int NW, bool VEC>
+// FULL selects the full-form epilogue (beta * old C, activation); the plain
+// one is a separate instantiation so that the main loop's register
+// allocation does not carry the larger epilogue.
+template <int AB, int CT, bool NT, int BM, int BN, int NW, bool VEC, bool FULL>
 __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
   constexpr int E = FmtBytes<AB>::value;
   constexpr int CE = FmtBytes<CT>::value;
@@ -666,16 +781,25 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
   static_assert(NW * 32 * stage_pitch<CT, BN / (NW / 2)>() <= 2 * STAGE, "epilogue staging");
   __syncthreads();
   char *C = (char *)p.C + z * p.strideC * CE;
-  store_tile_lds<CT, FM, FN>(acc, lds + wave * 32 * stage_pitch<CT, WTN>(), C, p.ldc, M, N,
-                             m0 + wm * WTM, n0 + wn * WTN, p.bias, AB == kF8 ? p.scale : 1.f,
-                             lane);
+  if constexpr (FULL) {
+    static_assert(NW * 16 * (WTN * 4 + 32) <= 2 * STAGE, "full-form epilogue staging");
+    store_tile_ex<CT, FM, FN>(acc, lds + wave * 16 * (WTN * 4 + 32), C, p.ldc, M, N, m0 + wm * WTM,
+                              n0 + wn * WTN, p.bias, p.scale, p.beta, p.act, lane);
+  } else {
+    store_tile_lds<CT, FM, FN>(acc, lds + wave * 32 * stage_pitch<CT, WTN>(), C, p.ldc, M, N,
+                               m0 + wm * WTM, n0 + wn * WTN, p.bias, p.scale, lane);
+  }
 }
 
 template <int AB, int CT, bool NT, int BM, int BN, int NW, bool VEC>
 hipError_t launch_one(const GemmParams &p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
-  hipLaunchKernelGGL((gemm_mfma_kernel<AB, CT, NT, BM, BN, NW, VEC>), dim3((unsigned)tiles),
-                     dim3(64 * NW), 0, stream, p);
+  if (p.beta != 0.f || p.act != 0)
+    hipLaunchKernelGGL((gemm_mfma_kernel<AB, CT, NT, BM, BN, NW, VEC, true>), dim3((unsigned)tiles),
+                       dim3(64 * NW), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_mfma_kernel<AB, CT, NT, BM, BN, NW, VEC, false>), dim3((unsigned)tiles),
+                       dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
 

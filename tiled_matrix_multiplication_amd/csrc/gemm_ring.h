@@ -97,7 +97,7 @@ __device__ __forceinline__ int nn_swz(int row) {
   return E == 2 ? 4 * (row & 3) : (row & 7);
 }
 
-template <int AB, int CT, bool NT, int NW>
+template <int AB, int CT, bool NT, int NW, bool FULL>
 __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   constexpr int BM = 256, BN = 256;
   constexpr int E = FmtBytes<AB>::value;
@@ -344,16 +344,25 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   char *C = (char *)p.C + z * p.strideC * CE;
   // the loop's last barrier follows every LDS read of the stages
   static_assert(NW * 32 * stage_pitch<CT, WTN>() <= kRingStages * STAGE, "epilogue staging");
-  store_tile_lds<CT, FM, FN>(acc, lds + wave * 32 * stage_pitch<CT, WTN>(), C, p.ldc, M, N,
-                             m0 + wm * WTM, n0 + wn * WTN, p.bias, AB == kF8 ? p.scale : 1.f,
-                             lane);
+  if constexpr (FULL) {
+    static_assert(NW * 16 * (WTN * 4 + 32) <= kRingStages * STAGE, "full-form epilogue staging");
+    store_tile_ex<CT, FM, FN>(acc, lds + wave * 16 * (WTN * 4 + 32), C, p.ldc, M, N, m0 + wm * WTM,
+                              n0 + wn * WTN, p.bias, p.scale, p.beta, p.act, lane);
+  } else {
+    store_tile_lds<CT, FM, FN>(acc, lds + wave * 32 * stage_pitch<CT, WTN>(), C, p.ldc, M, N,
+                               m0 + wm * WTM, n0 + wn * WTN, p.bias, p.scale, lane);
+  }
 }
 
 template <int AB, int CT, bool NT, int NW>
 hipError_t launch_ring(const GemmParams &p, hipStream_t stream) {
   const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-  hipLaunchKernelGGL((gemm_ring_kernel<AB, CT, NT, NW>), dim3((unsigned)tiles), dim3(64 * NW), 0,
-                     stream, p);
+  if (p.beta != 0.f || p.act != 0)
+    hipLaunchKernelGGL((gemm_ring_kernel<AB, CT, NT, NW, true>), dim3((unsigned)tiles), dim3(64 * NW), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((gemm_ring_kernel<AB, CT, NT, NW, false>), dim3((unsigned)tiles), dim3(64 * NW), 0,
+                       stream, p);
   return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@
 //   * the NW partial tiles are summed by a fixed tree through LDS (waves
 //     w and w + h for h = NW/2, NW/4, ..., 1; the result does not depend
 //     on timing), then scale, bias, one nearest-even rounding and row-wise
-//     stores.
+//     stores (in the full form also + beta * old C and ReLU before the
+//     rounding).
 // Rows past M (columns past N) read the last valid row and are not stored;
 // a K tail (K % 32) is read element by element with zero fill.
 #include <stdint.h>
@@ -230,6 +231,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(GemmParams p, i
       if (p.bias && gc + j < N) o[j] += p.bias[gc + j];
     }
     char *dst = Cz + (gr * p.ldc + gc) * CE;
+    if (p.beta != 0.f) {   // full form: + beta * old C
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (gc + j >= N) break;
+        if constexpr (CT == kF32)
+          o[j] += p.beta * ((const float *)dst)[j];
+        else if constexpr (CT == kBF16)
+          o[j] += p.beta * __uint_as_float((uint32_t)((const uint16_t *)dst)[j] << 16);
+        else
+          o[j] += p.beta * (float)__builtin_bit_cast(_Float16, ((const uint16_t *)dst)[j]);
+      }
+    }
+    if (p.act == 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = o[j] > 0.f ? o[j] : 0.f;
+    }
     if (vec_c && gc + 4 <= N) {
       if constexpr (CT == kF32)
         *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};

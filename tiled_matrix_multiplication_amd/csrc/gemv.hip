@@ -196,7 +196,16 @@ hipError_t launch_typed(bool vec, const GemvParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// ---- K == 0 fill for the GEMM: C = bias (or 0)
+// Value of a stored output element (the old C of the full form).
+template <int CT>
+__device__ __forceinline__ float get(const void *C, int64_t idx) {
+  if constexpr (CT == kF32) return ((const float *)C)[idx];
+  else if constexpr (CT == kBF16) return __uint_as_float((uint32_t)((const uint16_t *)C)[idx] << 16);
+  else return (float)__builtin_bit_cast(_Float16, ((const uint16_t *)C)[idx]);
+}
+
+// ---- K == 0 fill for the GEMM: C = act(bias + beta * old C), the empty
+// sum (bias and beta default to none: C = 0)
 template <int CT>
 __global__ __launch_bounds__(256) void fill_kernel(GemmParams p) {
   const int64_t per = p.M * p.N;
@@ -206,8 +215,10 @@ __global__ __launch_bounds__(256) void fill_kernel(GemmParams p) {
     const int64_t z = t / per;
     const int64_t rem = t - z * per;
     const int64_t row = rem / p.N, col = rem - row * p.N;
-    const float v = p.bias ? p.bias[col] : 0.f;
+    float v = p.bias ? p.bias[col] : 0.f;
     const int64_t idx = z * p.strideC + row * p.ldc + col;
+    if (p.beta != 0.f) v += p.beta * get<CT>(p.C, idx);
+    if (p.act == 1) v = v > 0.f ? v : 0.f;
     put<CT>(p.C, idx, v);
   }
 }

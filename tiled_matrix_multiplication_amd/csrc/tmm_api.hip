@@ -41,16 +41,29 @@ int64_t max1(int64_t v) { return v > 1 ? v : 1; }
 
 // Common checks of tmm_gemm and tmm_gemm_strided_batched.  Returns TMM_OK
 // and sets *quick when nothing is to be launched.
+// The full form's extra arguments (tmm_gemm_ex); the plain entry points
+// use alpha = scale_a * scale_b, beta = 0, no activation, trans_a = 0.
+struct Ex {
+  bool full = false;
+  int trans_a = 0;
+  float beta = 0.f;
+  int act = 0;
+};
+
 int check_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const void *A,
                int64_t lda, int64_t sA, const void *B, int64_t ldb, int64_t sB, const void *C,
                int64_t ldc, int64_t sC, int64_t batch, const float *bias, float scale_a,
-               float scale_b, bool *quick) {
+               float scale_b, const Ex &ex, bool *quick) {
   *quick = false;
   if (M < 0 || N < 0 || K < 0 || batch < 0) return TMM_ERR_DIM;
   if (!known_type(ab) || !known_type(c) || !pair_ok(ab, c)) return TMM_ERR_DTYPE;
-  if (!isfinite(scale_a) || !isfinite(scale_b)) return TMM_ERR_SCALE;
-  if (ab != TMM_F8E4M3 && (scale_a != 1.0f || scale_b != 1.0f)) return TMM_ERR_SCALE;
-  if (lda < max1(K) || ldb < max1(trans_b ? K : N) || ldc < max1(N)) return TMM_ERR_LD;
+  if (ex.trans_a && ab != TMM_BF16 && ab != TMM_F16) return TMM_ERR_DTYPE;
+  if (!isfinite(scale_a) || !isfinite(scale_b) || !isfinite(scale_a * scale_b) || !isfinite(ex.beta))
+    return TMM_ERR_SCALE;
+  if (!ex.full && ab != TMM_F8E4M3 && (scale_a != 1.0f || scale_b != 1.0f)) return TMM_ERR_SCALE;
+  if (ex.act != 0 && ex.act != 1) return TMM_ERR_ARG;
+  if (lda < max1(ex.trans_a ? M : K) || ldb < max1(trans_b ? K : N) || ldc < max1(N))
+    return TMM_ERR_LD;
   if (sA < 0 || sB < 0 || sC < 0) return TMM_ERR_STRIDE;
   if (M == 0 || N == 0 || batch == 0) {
     *quick = true;
@@ -66,7 +79,7 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, cons
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   if (tiles > (int64_t)0x7fffffff / batch) return TMM_ERR_DIM;
   // Kernels address A and B of one problem with 32-bit byte offsets.
-  if (K > 0 && (((M - 1) * lda + K) * e >= ((int64_t)1 << 32) ||
+  if (K > 0 && (((ex.trans_a ? (K - 1) * lda + M : (M - 1) * lda + K) * e) >= ((int64_t)1 << 32) ||
                 ((trans_b ? (N - 1) * ldb + K : (K - 1) * ldb + N) * e) >= ((int64_t)1 << 32)))
     return TMM_ERR_DIM;
   return TMM_OK;
@@ -90,10 +103,11 @@ int cu_count() {
 }
 
 // TMM_FORCE_TILE = "256x256" | "256x128" | "128x128" | "256x256w4" | "256x256s2" |
-// "256x256r" | "skinny" pins the tile shape for measurements and tile-by-tile
+// "256x256r" | "skinny" | "generic" pins the tile shape for measurements and tile-by-tile
 // tests ("256x256s2": 256x256 tiles on the two-stage kernel only; "256x256r":
 // on the ring kernel wherever it applies, K-contiguous B included; "skinny":
-// the skinny-M kernel wherever it applies, any M).
+// the skinny-M kernel wherever it applies, any M; "generic": the any-layout
+// kernel for 16-bit inputs).
 // Read on every call so that a test can switch it; anything else leaves the
 // choice to pick_tile.
 int forced_tile() {
@@ -189,10 +203,10 @@ hipError_t dispatch_gemm(int ab, int c, bool trans_b, tmm::Tile tile, bool vec,
 int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const void *A,
              int64_t lda, int64_t sA, const void *B, int64_t ldb, int64_t sB, void *C, int64_t ldc,
              int64_t sC, int64_t batch, const float *bias, float scale_a, float scale_b,
-             hipStream_t stream) {
+             hipStream_t stream, const Ex &ex = Ex()) {
   bool quick = false;
   const int rc = check_gemm(M, N, K, ab, c, trans_b, A, lda, sA, B, ldb, sB, C, ldc, sC, batch,
-                            bias, scale_a, scale_b, &quick);
+                            bias, scale_a, scale_b, ex, &quick);
   if (rc != TMM_OK || quick) return rc;
 
   tmm::GemmParams p;
@@ -203,11 +217,19 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
   p.bias = bias;
   p.scale = scale_a * scale_b;
   p.batch = batch;
+  p.beta = ex.beta;
+  p.act = ex.act;
+  const bool plain = p.scale == 1.f && p.beta == 0.f && p.act == 0;
 
   hipError_t err;
   if (K == 0) {
     err = tmm::launch_fill((Fmt)c, p, stream);
-  } else if (M == 1 && batch == 1 && trans_b && ab != TMM_F8E4M3 &&
+  } else if (ex.trans_a) {
+    const int e = elem_bytes(ab);
+    const bool va = aligned(A, 16) && (lda * e) % 16 == 0 && (batch == 1 || (sA * e) % 16 == 0);
+    const bool vb = aligned(B, 16) && (ldb * e) % 16 == 0 && (batch == 1 || (sB * e) % 16 == 0);
+    err = tmm::launch_gemm_generic((Fmt)ab, (Fmt)c, true, trans_b != 0, va, vb, p, stream);
+  } else if (M == 1 && batch == 1 && trans_b && ab != TMM_F8E4M3 && plain &&
              forced_tile() != tmm::kTileSkinny) {
     // y = W . x with W = B (N x K): the memory-bound matrix-vector path.
     tmm::GemvParams g;
@@ -227,7 +249,16 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
                      (trans_b || (N * e) % 16 == 0);
     const int f = forced_tile();
     const bool skinny_ok = vec && trans_b && (ab == TMM_BF16 || ab == TMM_F16);
-    if (skinny_ok && (f == tmm::kTileSkinny || (f < 0 && M <= kSkinnyMaxM))) {
+    const bool generic_forced = [] {
+      const char *s = getenv("TMM_FORCE_TILE");
+      return s && !strcmp(s, "generic");
+    }();
+    if (generic_forced && (ab == TMM_BF16 || ab == TMM_F16)) {
+      const int e = elem_bytes(ab);
+      const bool va = aligned(A, 16) && (lda * e) % 16 == 0 && (batch == 1 || (sA * e) % 16 == 0);
+      const bool vb = aligned(B, 16) && (ldb * e) % 16 == 0 && (batch == 1 || (sB * e) % 16 == 0);
+      err = tmm::launch_gemm_generic((Fmt)ab, (Fmt)c, false, trans_b != 0, va, vb, p, stream);
+    } else if (skinny_ok && (f == tmm::kTileSkinny || (f < 0 && M <= kSkinnyMaxM))) {
       int bm, bn;
       pick_skinny(M, N, batch, &bm, &bn);
       const int ce = elem_bytes(c);
@@ -250,6 +281,20 @@ int tmm_gemm(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type, tmm_dtype c_typ
              const float *bias, float scale_a, float scale_b, hipStream_t stream) {
   return run_gemm(M, N, K, ab_type, c_type, trans_b, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, bias,
                   scale_a, scale_b, stream);
+}
+
+int tmm_gemm_ex(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type, tmm_dtype c_type,
+                int trans_a, int trans_b, const void *A, int64_t lda, int64_t strideA,
+                const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc,
+                int64_t strideC, int64_t batch, const float *bias, float alpha, float beta,
+                int activation, hipStream_t stream) {
+  Ex ex;
+  ex.full = true;
+  ex.trans_a = trans_a != 0;
+  ex.beta = beta;
+  ex.act = activation;
+  return run_gemm(M, N, K, ab_type, c_type, trans_b, A, lda, strideA, B, ldb, strideB, C, ldc,
+                  strideC, batch, bias, alpha, 1.0f, stream, ex);
 }
 
 int tmm_gemm_strided_batched(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type,
@@ -335,10 +380,11 @@ const char *tmm_status_string(int status) {
     case TMM_ERR_LD: return "leading dimension smaller than the row length";
     case TMM_ERR_NULL: return "null pointer for an operand with non-zero extent";
     case TMM_ERR_DTYPE: return "unsupported element type or type combination";
-    case TMM_ERR_SCALE: return "scale must be finite, and 1 unless the inputs are fp8";
+    case TMM_ERR_SCALE: return "scale, alpha or beta not finite, or a scale != 1 for non-fp8 inputs";
     case TMM_ERR_STRIDE: return "negative batch stride or overlapping output matrices";
     case TMM_ERR_ALIGN: return "pointer not aligned to its element size";
     case TMM_ERR_LAUNCH: return "HIP reported an error at kernel launch";
+    case TMM_ERR_ARG: return "unknown activation code";
     default: return "unknown status code";
   }
 }

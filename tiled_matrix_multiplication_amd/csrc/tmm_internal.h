@@ -33,8 +33,10 @@ struct GemmParams {
   void *C;
   int64_t ldc, strideC;
   const float *bias;
-  float scale;      // scale_a * scale_b (1 unless fp8)
+  float scale;      // alpha: scale_a * scale_b (1 unless fp8) in the plain form
   int64_t batch;
+  float beta;       // full form: + beta * old C (0: C is not read)
+  int act;          // full form: 0 none, 1 ReLU, applied last
 };
 
 // Rows/columns of a workgroup tile.
@@ -64,7 +66,13 @@ hipError_t launch_gemm_f8(Fmt c, bool trans_b, Tile tile, bool vec, const GemmPa
 hipError_t launch_gemm_skinny(Fmt ab, Fmt c, int bm, int bn, bool vec_c, const GemmParams &p,
                               hipStream_t stream);
 
-// C = bias broadcast (or 0) for the K == 0 empty sum.
+// Any-layout GEMM (16-bit inputs; A may be stored K x M): 64 x 64 tiles.
+// vec_a / vec_b allow 16-byte loads (rows 16-byte aligned).
+hipError_t launch_gemm_generic(Fmt ab, Fmt c, bool trans_a, bool trans_b, bool vec_a, bool vec_b,
+                               const GemmParams &p, hipStream_t stream);
+
+// C = act(bias + beta * old C) (bias, beta default none) for the K == 0
+// empty sum.
 hipError_t launch_fill(Fmt c, const GemmParams &p, hipStream_t stream);
 
 struct GemvParams {
