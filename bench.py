@@ -94,11 +94,25 @@ WORKLOADS = {
     "skinny_m16": (16, 4096, 4096, 1, "f16", "f16", True, True),
     "skinny_m64": (64, 4096, 4096, 1, "f16", "f16", True, True),
     "skinny_m256": (256, 4096, 4096, 1, "f16", "f16", True, True),
+    # full BLAS form (tmm_gemm_ex), options in FULL_FORM below
+    "ffn_up_relu": (8192, 14336, 4096, 1, "bf16", "bf16", True, True),
+    "ffn_down_residual": (8192, 4096, 14336, 1, "bf16", "bf16", True, True),
+    "wgrad_qkv": (4096, 12288, 8192, 1, "bf16", "f32", False, False),
     # fused attention: (Nq queries, Nk keys, D head size, batch x heads, in, out, -, -)
     "attn_fused": (2048, 2048, 128, 128, "f16", "f16", True, False),
 }
 
 ATTENTION = ("attn_fused",)
+
+# Full-form options: a linear layer with a fused ReLU; FFN-down adding its
+# output onto the residual stream (beta = 1, C read); the weight gradient of
+# the QKV projection, dW = X^T . dY with X (tokens x in) stored as is
+# (trans_a), fp32 gradient.
+FULL_FORM = {
+    "ffn_up_relu": {"relu": True},
+    "ffn_down_residual": {"beta": 1.0},
+    "wgrad_qkv": {"trans_a": True},
+}
 
 
 def attention_flops(Nq, Nk, D, batch=1):
@@ -116,7 +130,10 @@ def work(name):
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
     if name in ATTENTION:
         return attention_flops(M, N, K, Z), attention_bytes(M, N, K, BYTES[fin], BYTES[fout], Z)
-    return gemm_flops(M, N, K, Z), gemm_bytes(M, N, K, BYTES[fin], BYTES[fout], Z, bias)
+    nbytes = gemm_bytes(M, N, K, BYTES[fin], BYTES[fout], Z, bias)
+    if FULL_FORM.get(name, {}).get("beta"):
+        nbytes += float(Z * M * N * BYTES[fout])   # the old C is read
+    return gemm_flops(M, N, K, Z), nbytes
 
 
 def describe(name):
@@ -125,6 +142,11 @@ def describe(name):
     b = f"batch {Z} x " if Z > 1 else ""
     if name == "gemv":
         return f"{fin} GEMV y = W.x + bias, W {N}x{K}, {fout} y"
+    if name in FULL_FORM:
+        o = FULL_FORM[name]
+        lay = ("T" if o.get("trans_a") else "N") + ("T" if tb else "N")
+        extra = (", ReLU" if o.get("relu") else "") + (f", + {o['beta']} C" if o.get("beta") else "")
+        return f"{fin} GEMM {M}x{N}x{K} {lay}, {fout} out{', fp32 bias' if bias else ''}{extra}"
     if name in ATTENTION:
         return (f"{fin} fused attention softmax(Q K^T/sqrt(D)) V, batch x heads {Z}, "
                 f"{M} queries x {N} keys, head size {K}, {fout} out")
@@ -146,6 +168,14 @@ def make_inputs(name, copies, dev):
         sets = [(hQ.to(dev), hK.to(dev), hV.to(dev), torch.empty((Z, M, K), dtype=tdt, device=dev))
                 for _ in range(copies)]
         return sets, None, (Q, Kt, V, 1.0, 1.0)
+    if name in FULL_FORM and FULL_FORM[name].get("trans_a"):
+        xa = syn.normal((K, M), syn.seed_of(8, "A"))   # stored K x M (tokens x in)
+        xb = syn.normal((K, N), syn.seed_of(8, "B"))
+        A, B = syn.to_bits(xa, fin), syn.to_bits(xb, fin)
+        hA, hB = syn.as_torch(A, fin), syn.as_torch(B, fin)
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[fout]
+        sets = [(hA.to(dev), hB.to(dev), torch.empty((M, N), dtype=tdt, device=dev)) for _ in range(copies)]
+        return sets, None, (A, B, None, 1.0, 1.0)
     cfg = {"square_bf16": 2, "qkv": 3, "ffn_up": 3, "ffn_down": 3, "gemv": 3, "attn_scores": 4,
            "attn_output": 4, "fp8_square": 5}.get(name, 7 if name.startswith("skinny") else 5)
     ashape = (Z, M, K) if Z > 1 else (M, K)
@@ -173,12 +203,23 @@ def make_inputs(name, copies, dev):
         dC = torch.empty((Z, M, N) if Z > 1 else (M, N), dtype=tdt, device=dev)
         sets.append((dA, dB, dC))
     dbias = torch.from_numpy(bvec).to(dev) if bvec is not None else None
+    if FULL_FORM.get(name, {}).get("beta"):
+        for _, _, dC in sets:   # an old C to add onto (the residual stream)
+            dC.copy_(torch.randn(dC.shape, device=dev).to(dC.dtype))
     return sets, dbias, (A, B, bvec, float(sa), float(sb))
 
 
 def launcher(name, sets, dbias, sa, sb):
     import tiled_matrix_multiplication_amd as tmm
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    if name in FULL_FORM:
+        o = FULL_FORM[name]
+
+        def run(i):
+            A, B, C = sets[i % len(sets)]
+            tmm.tmm_gemm_ex(A, B, C, bias=dbias, trans_a=o.get("trans_a", False), trans_b=tb,
+                            beta=o.get("beta", 0.0), relu=o.get("relu", False))
+        return run
     if name in ATTENTION:
         scale = float(K) ** -0.5
 
@@ -442,6 +483,8 @@ def cpu_baseline(name, r, target_s=20.0):
     import oracle
     if name in ATTENTION:
         return cpu_baseline_attention(name, r, target_s)
+    if name in FULL_FORM:
+        return cpu_baseline_full(name, r, target_s)
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
     A, B, bvec, sa, sb = r["host"]
     if Z > 1:
@@ -475,6 +518,40 @@ def cpu_baseline(name, r, target_s=20.0):
             "sample": (f"{len(idx)} of {M} rows" if len(idx) < M else f"all {M} rows") +
                       f" of the {describe(name)} product ({len(idx)}x{N}x{K}, fp64 triple loop; "
                       f"time includes decoding the inputs)",
+            "sample_rel_fro_vs_gpu": err}
+
+
+def cpu_baseline_full(name, r, target_s=20.0):
+    """The oracle's full form on a row sample (rows of op(A)).  The sample is
+    compared with the GPU rows unless beta != 0 (the timed launches kept
+    adding onto C, so the GPU's C is not one launch's result)."""
+    import oracle
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    o = FULL_FORM[name]
+    A, B, bvec, sa, sb = r["host"]
+    ta = o.get("trans_a", False)
+    rng = np.random.default_rng(12345)
+
+    def run_rows(rows):
+        idx = np.sort(rng.choice(M, size=rows, replace=False))
+        a = np.ascontiguousarray(A[:, idx] if ta else A[idx])
+        cin = np.zeros((rows, N)) if o.get("beta") else None
+        t0 = time.perf_counter()
+        out = oracle.gemm_ex(fin, a, B, ta, tb, 1.0, o.get("beta", 0.0), cin, bvec, o.get("relu", False))
+        return idx, out, time.perf_counter() - t0
+
+    idx, out, t8 = run_rows(8)
+    idx, out, t64 = run_rows(64)
+    per_row = max((t64 - t8) / 56, 1e-6)
+    rows = int(min(M, max(64, (target_s - t8) / per_row)))
+    t = t64
+    if rows > len(idx):
+        idx, out, t = run_rows(rows)
+    err = None if o.get("beta") else compare_rows(r["sets"][0][2], idx, out)
+    return {"value": round(gemm_flops(len(idx), N, K) / t / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.threads(), "kind": "oracle", "seconds": round(t, 2),
+            "sample": f"{len(idx)} of {M} rows of the {describe(name)} product (fp64; time includes "
+                      f"decoding the inputs)",
             "sample_rel_fro_vs_gpu": err}
 
 
