@@ -62,11 +62,13 @@ def _load():
                                 ctypes.c_int, vp, dp, dp, vp, i64, vp]
     lib.oracle_gemm_ex.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64,
                                    vp, i64, dp, dp, vp, vp, ctypes.c_int, vp, i64, vp]
+    lib.oracle_conv2d.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp,
+                                  ctypes.c_int, ctypes.c_int, vp, vp]
     lib.oracle_threads.argtypes = []
     lib.oracle_attention.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, vp, i64, vp, i64,
                                      ctypes.c_double, vp, i64, vp]
     for f in (lib.oracle_decode, lib.oracle_round, lib.oracle_gemm, lib.oracle_threads,
-              lib.oracle_attention, lib.oracle_gemm_ex):
+              lib.oracle_attention, lib.oracle_gemm_ex, lib.oracle_conv2d):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -182,6 +184,39 @@ def gemm_ex(fmt, A: np.ndarray, B: np.ndarray, trans_a: bool = False, trans_b: b
     if rc:
         raise ValueError(f"oracle_gemm_ex failed ({rc})")
     return (C, T) if want_abs else C
+
+
+def conv2d(fmt, x: np.ndarray, w: np.ndarray, pad: int, scale: np.ndarray | None = None,
+           bias: np.ndarray | None = None, relu: bool = False, pool: int = 1,
+           want_abs: bool = False):
+    """Fused stride-1 convolution in float64: act(conv(x, w) * scale + bias),
+    max-pooled over 2 x 2 blocks when ``pool`` == 2.
+
+    x: (N, H, W, C) bit patterns (NHWC); w: (K, R, S, C); zero padding ``pad``.
+    Returns (N, OH, OW, K) float64, with ``want_abs`` also the |.| companion
+    of each selected output.
+    """
+    f = _fmt(fmt)
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    if x.dtype != _BITS[f] or w.dtype != _BITS[f] or x.ndim != 4 or w.ndim != 4:
+        raise TypeError("x and w must be 4-D arrays of the format's bit patterns")
+    N, H, W, C = x.shape
+    K, R, S, C2 = w.shape
+    if C2 != C:
+        raise ValueError("channel counts differ")
+    P, Q = H + 2 * pad - R + 1, W + 2 * pad - S + 1
+    if P < 1 or Q < 1 or (pool == 2 and (P % 2 or Q % 2)):
+        raise ValueError("output size not positive (or not even for pooling)")
+    sc = None if scale is None else np.ascontiguousarray(scale, dtype=np.float32)
+    bi = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty((N, P // pool, Q // pool, K), dtype=np.float64)
+    T = np.empty_like(out) if want_abs else None
+    rc = _load().oracle_conv2d(N, H, W, C, K, R, S, pad, f, _ptr(x), _ptr(w), _ptr(sc), _ptr(bi),
+                               1 if relu else 0, int(pool), _ptr(out), _ptr(T))
+    if rc:
+        raise ValueError(f"oracle_conv2d failed ({rc})")
+    return (out, T) if want_abs else out
 
 
 def attention(fmt, Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,

@@ -36,7 +36,8 @@
  *
  * oracle_gemm_ex states the full BLAS form the same way (see there).
  *
- * oracle_attention states softmax(scale Q K^T) V the same way (see there).
+ * oracle_attention states softmax(scale Q K^T) V the same way (see there),
+ * and oracle_conv2d the fused convolution (see there).
  *
  * Each pin of this file lives in tests/test_oracle.py.
  */
@@ -421,6 +422,81 @@ int oracle_attention(int64_t Nq, int64_t Nk, int64_t D, int fmt, const void *Q,
 }
 
 /* Number of threads the product above runs on. */
+
+/*
+ * Direct 2-D convolution with the fused epilogue, stride 1:
+ *
+ *   conv[n][y][x][f] = sum_{r<R, s<S, c<C} w[f][r][s][c] * in[n][y+r-pad][x+s-pad][c]
+ *                      (inputs outside the H x W image are 0)
+ *   v = act(conv * scale[f] + bias[f]);  out = v, or the max of v over each
+ *   2 x 2 block (y, x) in {2Y, 2Y+1} x {2X, 2X+1} when pool == 2
+ *
+ * CMU 15-418 Lecture 27 notes: the convolution as the seven-loop nest of
+ * section 2.2 and the conv_fused listing of section 3.1 (NHWC input with a
+ * zero halo of `pad`, weights [K][R][S][C], per-filter scale and bias,
+ * ReLU, 2 x 2 max pooling), in the listing's loop order over (dy, dx, r, s,
+ * c) for each pooled output.  The implicit-GEMM view (section 2.3) is not
+ * used here: this is the definition.
+ *
+ *   in  : N x H x W x C inputs (format fmt), NHWC, contiguous
+ *   w   : K x R x S x C inputs, contiguous
+ *   out : N x OH x OW x K doubles, OH = (H + 2 pad - R + 1) / pool (same for W)
+ *   T   : NULL or like out: the |.| companion of the selected (pre-pool)
+ *         output, |scale| sum |w in| + |bias|
+ */
+int oracle_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+                  int64_t pad, int fmt, const void *in, const void *w, const float *scale,
+                  const float *bias, int relu, int pool, double *out, double *T) {
+  if (N < 0 || H < 1 || W < 1 || C < 1 || K < 1 || R < 1 || S < 1 || pad < 0 ||
+      fmt < ORC_F32 || fmt > ORC_E4M3 || (pool != 1 && pool != 2))
+    return -1;
+  const int64_t P = H + 2 * pad - R + 1, Q = W + 2 * pad - S + 1;
+  if (P < 1 || Q < 1 || (pool == 2 && (P % 2 || Q % 2)))
+    return -2;
+  const int64_t OH = P / pool, OW = Q / pool;
+  int fail = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t oy = 0; oy < OH; ++oy) {
+      for (int64_t ox = 0; ox < OW; ++ox)
+        for (int64_t f = 0; f < K; ++f) {
+          double best = 0.0, best_t = 0.0;
+          int first = 1;
+          for (int64_t dy = 0; dy < pool; ++dy)
+            for (int64_t dx = 0; dx < pool; ++dx) {
+              const int64_t y = oy * pool + dy, x = ox * pool + dx;
+              double acc = 0.0, tab = 0.0;
+              for (int64_t r = 0; r < R; ++r)
+                for (int64_t s = 0; s < S; ++s) {
+                  const int64_t iy = y + r - pad, ix = x + s - pad;
+                  if (iy < 0 || iy >= H || ix < 0 || ix >= W)
+                    continue;
+                  for (int64_t c = 0; c < C; ++c) {
+                    const double t = dec_at(fmt, w, ((f * R + r) * S + s) * C + c) *
+                                     dec_at(fmt, in, ((n * H + iy) * W + ix) * C + c);
+                    acc += t;
+                    tab += fabs(t);
+                  }
+                }
+              const double sc = scale ? (double)scale[f] : 1.0;
+              const double b = bias ? (double)bias[f] : 0.0;
+              double v = acc * sc + b;
+              if (relu && !(v > 0.0))
+                v = 0.0;
+              if (first || v > best) {
+                best = v;
+                best_t = fabs(sc) * tab + fabs(b);
+              }
+              first = 0;
+            }
+          out[((n * OH + oy) * OW + ox) * K + f] = best;
+          if (T)
+            T[((n * OH + oy) * OW + ox) * K + f] = best_t;
+        }
+    }
+  return fail ? -3 : 0;
+}
+
 int oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
