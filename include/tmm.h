@@ -93,7 +93,7 @@ enum tmm_status {
   TMM_ERR_STRIDE = -6, /* negative batch stride, or C matrices that overlap   */
   TMM_ERR_ALIGN = -7,  /* pointer not aligned to its element size            */
   TMM_ERR_LAUNCH = -8, /* HIP reported an error at launch                     */
-  TMM_ERR_ARG = -9     /* unknown activation code                            */
+  TMM_ERR_ARG = -9     /* unknown activation code or pooling factor          */
 };
 
 /* Activation applied last by tmm_gemm_ex. */
@@ -194,6 +194,32 @@ int tmm_gemm_ex(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type, tmm_dtype c_
                 const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc,
                 int64_t strideC, int64_t batch, const float *bias, float alpha, float beta,
                 int activation, hipStream_t stream);
+
+/*
+ * Fused stride-1 2-D convolution, NHWC, as an implicit GEMM:
+ *   out[n][oy][ox][f] = pool over the 2 x 2 block of (y, x) (pool == 2) or
+ *   (y, x) = (oy, ox) (pool == 1) of
+ *     act( scale[f] * sum_{r,s,c} w[f][r][s][c] in[n][y+r-pad][x+s-pad][c] + bias[f] )
+ * with inputs outside the H x W image taken as 0.  (CMU 15-418 Lecture 27
+ * notes: the convolution loop nest of section 2.2, implicit GEMM in section
+ * 2.3, and the conv_fused listing of section 3.1 -- NHWC input with a zero
+ * halo, weights [K][R][S][C], per-filter scale and bias, ReLU, 2 x 2 max
+ * pooling.)
+ *   in : N x H x W x C, contiguous; w : K x R x S x C, contiguous; out :
+ *   N x OH x OW x K, contiguous, OH = (H + 2 pad - R + 1) / pool, OW alike.
+ *   scale, bias: K floats each or NULL (1 and 0).  in_type TMM_BF16 or
+ *   TMM_F16 (in and w alike), out_type in_type or TMM_F32; sums in fp32, one
+ *   nearest-even rounding after the pooling.
+ *   Limits: C a multiple of 8 and in, w 16-byte aligned (TMM_ERR_ALIGN);
+ *   N >= 0, H, W, C, K, R, S >= 1, pad >= 0, output size >= 1 and even
+ *   when pool == 2, R*S*C and every dimension below 2^31 (TMM_ERR_DIM);
+ *   pool 1 or 2 and activation TMM_ACT_NONE / TMM_ACT_RELU (TMM_ERR_ARG).
+ *   Quick return for N == 0.
+ */
+int tmm_conv2d_fused(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+                     int64_t pad, tmm_dtype in_type, tmm_dtype out_type, const void *in,
+                     const void *w, const float *scale, const float *bias, int activation,
+                     int pool, void *out, hipStream_t stream);
 
 /* Static English text of a status code (never NULL). */
 const char *tmm_status_string(int status);

@@ -194,7 +194,7 @@ def conv2d(fmt, x: np.ndarray, w: np.ndarray, pad: int, scale: np.ndarray | None
 
     x: (N, H, W, C) bit patterns (NHWC); w: (K, R, S, C); zero padding ``pad``.
     Returns (N, OH, OW, K) float64, with ``want_abs`` also the |.| companion
-    of each selected output.
+    (the largest over each pooling window).
     """
     f = _fmt(fmt)
     x = np.ascontiguousarray(x)

@@ -441,8 +441,9 @@ int oracle_attention(int64_t Nq, int64_t Nk, int64_t D, int fmt, const void *Q,
  *   in  : N x H x W x C inputs (format fmt), NHWC, contiguous
  *   w   : K x R x S x C inputs, contiguous
  *   out : N x OH x OW x K doubles, OH = (H + 2 pad - R + 1) / pool (same for W)
- *   T   : NULL or like out: the |.| companion of the selected (pre-pool)
- *         output, |scale| sum |w in| + |bias|
+ *   T   : NULL or like out: |scale| sum |w in| + |bias| of the output, the
+ *         largest over the pooling window (the error of a max is at most
+ *         the largest error of its candidates)
  */
 int oracle_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
                   int64_t pad, int fmt, const void *in, const void *w, const float *scale,
@@ -483,10 +484,11 @@ int oracle_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t
               double v = acc * sc + b;
               if (relu && !(v > 0.0))
                 v = 0.0;
-              if (first || v > best) {
+              if (first || v > best)
                 best = v;
-                best_t = fabs(sc) * tab + fabs(b);
-              }
+              const double tv = fabs(sc) * tab + fabs(b);
+              if (first || tv > best_t)
+                best_t = tv;
               first = 0;
             }
           out[((n * OH + oy) * OW + ox) * K + f] = best;

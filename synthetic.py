@@ -51,6 +51,13 @@ def normal(shape, seed: int, std: float = 1.0, rows=None) -> np.ndarray:
     return _blocked(shape, seed, rows, lambda g, n: g.standard_normal(n, dtype=np.float32) * np.float32(std))
 
 
+def uniform(shape, seed: int, lo: float = -0.5, hi: float = 0.5, rows=None) -> np.ndarray:
+    """float32 uniform in [lo, hi) (the conv_fused listing's rand()/RAND_MAX - 0.5)."""
+    shape = tuple(int(s) for s in shape)
+    return _blocked(shape, seed, rows,
+                    lambda g, n: (g.random(n, dtype=np.float32) * np.float32(hi - lo) + np.float32(lo)))
+
+
 def small_ints(shape, seed: int, lo: int = -4, hi: int = 4, rows=None) -> np.ndarray:
     """float32 integers drawn uniformly from {lo, ..., hi}."""
     shape = tuple(int(s) for s in shape)

@@ -19,13 +19,13 @@ def tmm():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tmm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tmm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemm_ex", "tmm_gemv", "tmm_attention_fwd",
-         "tmm_status_string", "tmm_version"])
+         "tmm_conv2d_fused", "tmm_status_string", "tmm_version"])
 
 
 def test_library_exports_every_declared_symbol(tmm):
@@ -194,3 +194,27 @@ def test_gemm_ex_validation(tmm):
 def test_gemm_ex_quick_returns(tmm):
     assert gex(tmm, M=0, A=None, B=None, C=None) == 0
     assert gex(tmm, batch=0, A=None, B=None, C=None) == 0
+
+
+def conv(tmm, N=2, H=8, W=8, C=16, K=8, R=3, S=3, pad=1, it=1, ot=1, x=FAKE, w=FAKE2, out=FAKE3,
+         act=0, pool=1):
+    return tmm.lib.tmm_conv2d_fused(N, H, W, C, K, R, S, pad, it, ot, x, w, None, None, act, pool,
+                                    out, None)
+
+
+def test_conv_validation(tmm):
+    """Every call here fails a check before anything is launched."""
+    assert conv(tmm, C=12) == -7                    # channels not a multiple of 8
+    assert conv(tmm, pool=3) == -9
+    assert conv(tmm, act=4) == -9
+    assert conv(tmm, it=0, ot=0) == -4              # fp32 inputs are not accepted
+    assert conv(tmm, it=1, ot=2) == -4
+    assert conv(tmm, H=7, pool=2) == -1             # odd output cannot be pooled 2 x 2
+    assert conv(tmm, R=11, pad=0) == -1             # filter larger than the padded image
+    assert conv(tmm, H=0) == -1
+    assert conv(tmm, x=None) == -3
+    assert conv(tmm, x=ctypes.c_void_p(0x100008)) == -7   # input not 16-byte aligned
+
+
+def test_conv_quick_return(tmm):
+    assert conv(tmm, N=0, x=None, w=None, out=None) == 0

@@ -25,6 +25,7 @@ STATUS = {
 }
 
 EXPORTS = ("tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemm_ex", "tmm_gemv", "tmm_attention_fwd",
+           "tmm_conv2d_fused",
            "tmm_status_string", "tmm_version")
 
 _DTYPE = {torch.float32: TMM_F32, torch.bfloat16: TMM_BF16, torch.float16: TMM_F16,
@@ -47,6 +48,8 @@ def _load() -> ctypes.CDLL:
     lib.tmm_gemm_strided_batched.argtypes = [i64, i64, i64, ci, ci, ci, vp, i64, i64, vp, i64, i64,
                                              vp, i64, i64, i64, vp, cf, cf, vp]
     lib.tmm_gemv.argtypes = [i64, i64, ci, ci, vp, i64, vp, vp, vp, vp]
+    lib.tmm_conv2d_fused.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, ci, ci, vp, vp, vp, vp,
+                                     ci, ci, vp, vp]
     lib.tmm_gemm_ex.argtypes = [i64, i64, i64, ci, ci, ci, ci, vp, i64, i64, vp, i64, i64, vp, i64,
                                 i64, i64, vp, cf, cf, ci, vp]
     lib.tmm_attention_fwd.argtypes = [i64, i64, i64, i64, ci, ci, vp, i64, i64, vp, i64, i64,
@@ -55,7 +58,7 @@ def _load() -> ctypes.CDLL:
     lib.tmm_status_string.restype = ctypes.c_char_p
     lib.tmm_version.argtypes = []
     for f in (lib.tmm_gemm, lib.tmm_gemm_strided_batched, lib.tmm_gemm_ex, lib.tmm_gemv,
-              lib.tmm_attention_fwd,
+              lib.tmm_attention_fwd, lib.tmm_conv2d_fused,
               lib.tmm_version):
         f.restype = ci
     return lib
@@ -218,3 +221,31 @@ def tmm_attention_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torc
                                ctypes.c_void_p(_stream(stream)))
     _check("tmm_attention_fwd", rc)
     return O
+
+
+def tmm_conv2d_fused(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor, pad: int,
+                     scale: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+                     relu: bool = False, pool: int = 1, stream=None):
+    """out = pool(act(conv(x, w) * scale + bias)), stride 1, NHWC.
+
+    x (N, H, W, C), w (K, R, S, C), out (N, OH, OW, K), all contiguous;
+    scale / bias float32 (K,) or None; pool 1 or 2 (2 x 2 max)."""
+    _on_gpu(x, w, out, scale, bias)
+    for t in (x, w, out):
+        if not t.is_contiguous():
+            raise ValueError("x, w and out must be contiguous")
+    N, H, W, C = x.shape
+    K, R, S, C2 = w.shape
+    if C2 != C or w.dtype != x.dtype:
+        raise ValueError("x and w disagree in channels or element type")
+    P, Q = H + 2 * pad - R + 1, W + 2 * pad - S + 1
+    if tuple(out.shape) != (N, P // pool, Q // pool, K):
+        raise ValueError(f"out must be {(N, P // pool, Q // pool, K)}, got {tuple(out.shape)}")
+    for v in (scale, bias):
+        if v is not None and (v.dtype != torch.float32 or v.shape != (K,) or v.stride(0) != 1):
+            raise ValueError("scale and bias must be contiguous float32 vectors of K entries")
+    rc = lib.tmm_conv2d_fused(N, H, W, C, K, R, S, pad, _dtype(x), _dtype(out), _ptr(x), _ptr(w),
+                              _ptr(scale), _ptr(bias), 1 if relu else 0, int(pool), _ptr(out),
+                              ctypes.c_void_p(_stream(stream)))
+    _check("tmm_conv2d_fused", rc)
+    return out

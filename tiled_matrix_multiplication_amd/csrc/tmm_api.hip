@@ -373,6 +373,37 @@ int tmm_attention_fwd(int64_t batch, int64_t Nq, int64_t Nk, int64_t D, tmm_dtyp
   return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
 }
 
+int tmm_conv2d_fused(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+                     int64_t pad, tmm_dtype in_type, tmm_dtype out_type, const void *in,
+                     const void *w, const float *scale, const float *bias, int activation,
+                     int pool, void *out, hipStream_t stream) {
+  const int64_t big = (int64_t)1 << 31;
+  if (N < 0 || H < 1 || W < 1 || C < 1 || K < 1 || R < 1 || S < 1 || pad < 0) return TMM_ERR_DIM;
+  if (H >= big || W >= big || C >= big || K >= big || R >= big || S >= big || pad >= big ||
+      R * S * C >= big)
+    return TMM_ERR_DIM;
+  if ((in_type != TMM_BF16 && in_type != TMM_F16) || (out_type != in_type && out_type != TMM_F32))
+    return TMM_ERR_DTYPE;
+  if (activation != TMM_ACT_NONE && activation != TMM_ACT_RELU) return TMM_ERR_ARG;
+  if (pool != 1 && pool != 2) return TMM_ERR_ARG;
+  const int64_t P = H + 2 * pad - R + 1, Q = W + 2 * pad - S + 1;
+  if (P < 1 || Q < 1 || (pool == 2 && (P % 2 || Q % 2))) return TMM_ERR_DIM;
+  if (N == 0) return TMM_OK;
+  if (!in || !w || !out) return TMM_ERR_NULL;
+  if (C % 8 || !aligned(in, 16) || !aligned(w, 16) || !aligned(out, elem_bytes(out_type)) ||
+      (scale && !aligned(scale, 4)) || (bias && !aligned(bias, 4)))
+    return TMM_ERR_ALIGN;
+  const int64_t tiles = ((N * P * Q + 127) / 128) * ((K + 63) / 64);
+  if (N * P * Q >= ((int64_t)1 << 40) || tiles >= big) return TMM_ERR_DIM;
+
+  tmm::ConvParams p;
+  p.N = N; p.H = (int)H; p.W = (int)W; p.C = (int)C; p.K = (int)K; p.R = (int)R; p.S = (int)S;
+  p.pad = (int)pad; p.pool = pool; p.relu = activation == TMM_ACT_RELU ? 1 : 0;
+  p.in = in; p.w = w; p.scale = scale; p.bias = bias; p.out = out;
+  const hipError_t err = tmm::launch_conv((Fmt)in_type, (Fmt)out_type, p, stream);
+  return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
+}
+
 const char *tmm_status_string(int status) {
   switch (status) {
     case TMM_OK: return "success";
@@ -384,7 +415,7 @@ const char *tmm_status_string(int status) {
     case TMM_ERR_STRIDE: return "negative batch stride or overlapping output matrices";
     case TMM_ERR_ALIGN: return "pointer not aligned to its element size";
     case TMM_ERR_LAUNCH: return "HIP reported an error at kernel launch";
-    case TMM_ERR_ARG: return "unknown activation code";
+    case TMM_ERR_ARG: return "unknown activation code or pooling factor";
     default: return "unknown status code";
   }
 }

@@ -99,6 +99,21 @@ struct AttnParams {
   float scale_log2;  // scale * log2(e): scores go through exp2
 };
 
+// Fused stride-1 convolution, NHWC: out = pool(act(conv(in, w) * scale +
+// bias)); in N x H x W x C, w K x R x S x C, out N x (P/pool) x (Q/pool) x K
+// with P = H + 2 pad - R + 1, Q = W + 2 pad - S + 1; C % 8 == 0.
+struct ConvParams {
+  int64_t N;
+  int H, W, C, K, R, S, pad, pool, relu;
+  const void *in;
+  const void *w;
+  const float *scale;
+  const float *bias;
+  void *out;
+};
+
+hipError_t launch_conv(Fmt in, Fmt out, const ConvParams &p, hipStream_t stream);
+
 // Fused attention forward (attention.hip); D is 64 or 128, in is kF16 or
 // kBF16, out is in or kF32 (the host has checked all of it).
 hipError_t launch_attention(Fmt in, Fmt out, int D, const AttnParams &p, hipStream_t stream);
