@@ -98,11 +98,24 @@ WORKLOADS = {
     "ffn_up_relu": (8192, 14336, 4096, 1, "bf16", "bf16", True, True),
     "ffn_down_residual": (8192, 4096, 14336, 1, "bf16", "bf16", True, True),
     "wgrad_qkv": (4096, 12288, 8192, 1, "bf16", "f32", False, False),
+    # fused convolution as an implicit GEMM: (GEMM rows = pixels, filters,
+    # R S C, 1, in, out, -, -); the full shape is in CONV below
+    "conv_listing": (8 * 64 * 64, 64, 9 * 32, 1, "bf16", "f32", True, True),
+    "conv_large": (64 * 64 * 64, 128, 9 * 64, 1, "bf16", "bf16", True, True),
     # fused attention: (Nq queries, Nk keys, D head size, batch x heads, in, out, -, -)
     "attn_fused": (2048, 2048, 128, 128, "f16", "f16", True, False),
 }
 
 ATTENTION = ("attn_fused",)
+
+# Fused stride-1 convolutions (NHWC): the conv_fused listing's problem of the
+# Lecture 27 notes (batch 8, 64 x 64, 32 -> 64 channels, 3 x 3, one-pixel
+# halo, scale 1 + 0.01 f, bias 0.5, ReLU, 2 x 2 max pool; bf16 inputs, fp32
+# output as there) and the same layer at batch 64 with 64 -> 128 channels.
+CONV = {
+    "conv_listing": dict(N=8, H=64, W=64, C=32, K=64, R=3, S=3, pad=1, pool=2),
+    "conv_large": dict(N=64, H=64, W=64, C=64, K=128, R=3, S=3, pad=1, pool=2),
+}
 
 # Full-form options: a linear layer with a fused ReLU; FFN-down adding its
 # output onto the residual stream (beta = 1, C read); the weight gradient of
@@ -130,6 +143,13 @@ def work(name):
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
     if name in ATTENTION:
         return attention_flops(M, N, K, Z), attention_bytes(M, N, K, BYTES[fin], BYTES[fout], Z)
+    if name in CONV:
+        c = CONV[name]
+        OH = (c["H"] + 2 * c["pad"] - c["R"] + 1) // c["pool"]
+        OW = (c["W"] + 2 * c["pad"] - c["S"] + 1) // c["pool"]
+        nbytes = (c["N"] * c["H"] * c["W"] * c["C"] + c["K"] * c["R"] * c["S"] * c["C"]) * BYTES[fin] \
+            + c["N"] * OH * OW * c["K"] * BYTES[fout] + 8 * c["K"]
+        return gemm_flops(M, N, K), float(nbytes)
     nbytes = gemm_bytes(M, N, K, BYTES[fin], BYTES[fout], Z, bias)
     if FULL_FORM.get(name, {}).get("beta"):
         nbytes += float(Z * M * N * BYTES[fout])   # the old C is read
@@ -142,6 +162,10 @@ def describe(name):
     b = f"batch {Z} x " if Z > 1 else ""
     if name == "gemv":
         return f"{fin} GEMV y = W.x + bias, W {N}x{K}, {fout} y"
+    if name in CONV:
+        c = CONV[name]
+        return (f"{fin} fused conv NHWC {c['N']}x{c['H']}x{c['W']}x{c['C']} -> {c['K']}, "
+                f"{c['R']}x{c['S']} pad {c['pad']}, scale+bias+ReLU+{c['pool']}x{c['pool']} max pool, {fout} out")
     if name in FULL_FORM:
         o = FULL_FORM[name]
         lay = ("T" if o.get("trans_a") else "N") + ("T" if tb else "N")
@@ -168,6 +192,19 @@ def make_inputs(name, copies, dev):
         sets = [(hQ.to(dev), hK.to(dev), hV.to(dev), torch.empty((Z, M, K), dtype=tdt, device=dev))
                 for _ in range(copies)]
         return sets, None, (Q, Kt, V, 1.0, 1.0)
+    if name in CONV:
+        c = CONV[name]
+        x = syn.to_bits(syn.uniform((c["N"], c["H"], c["W"], c["C"]), syn.seed_of(9, "A")), fin)
+        w = syn.to_bits(syn.uniform((c["K"], c["R"], c["S"], c["C"]), syn.seed_of(9, "B")), fin)
+        sc = (1.0 + 0.01 * np.arange(c["K"])).astype(np.float32)
+        bi = np.full(c["K"], 0.5, dtype=np.float32)
+        OH = (c["H"] + 2 * c["pad"] - c["R"] + 1) // c["pool"]
+        OW = (c["W"] + 2 * c["pad"] - c["S"] + 1) // c["pool"]
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[fout]
+        hx, hw = syn.as_torch(x, fin), syn.as_torch(w, fin)
+        sets = [(hx.to(dev), hw.to(dev), torch.empty((c["N"], OH, OW, c["K"]), dtype=tdt, device=dev))
+                for _ in range(copies)]
+        return sets, (torch.from_numpy(sc).to(dev), torch.from_numpy(bi).to(dev)), (x, w, (sc, bi), 1.0, 1.0)
     if name in FULL_FORM and FULL_FORM[name].get("trans_a"):
         xa = syn.normal((K, M), syn.seed_of(8, "A"))   # stored K x M (tokens x in)
         xb = syn.normal((K, N), syn.seed_of(8, "B"))
@@ -212,6 +249,14 @@ def make_inputs(name, copies, dev):
 def launcher(name, sets, dbias, sa, sb):
     import tiled_matrix_multiplication_amd as tmm
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    if name in CONV:
+        c = CONV[name]
+        sc, bi = dbias
+
+        def run(i):
+            x, w, out = sets[i % len(sets)]
+            tmm.tmm_conv2d_fused(x, w, out, c["pad"], scale=sc, bias=bi, relu=True, pool=c["pool"])
+        return run
     if name in FULL_FORM:
         o = FULL_FORM[name]
 
@@ -316,7 +361,8 @@ def time_graph(run, launches, replays, warmup):
 def copies_for(name):
     """Enough distinct input copies that a launch finds its operands out of the MALL."""
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
-    per = work(name)[1] if name in ATTENTION else Z * ((M * K + K * N) * BYTES[fin] + M * N * BYTES[fout])
+    per = work(name)[1] if (name in ATTENTION or name in CONV) \
+        else Z * ((M * K + K * N) * BYTES[fin] + M * N * BYTES[fout])
     return int(max(1, min(20, np.ceil(600e6 / per))))
 
 
@@ -343,7 +389,7 @@ def measure(name, steps, warmup, dev):
     flops, nbytes = work(name)
     out = {"ms": ms, "wall": wall, "flops": flops, "bytes": nbytes, "copies": copies,
            "sets": sets, "host": host}
-    if name == "gemv" or name.startswith("skinny"):
+    if name == "gemv" or name.startswith("skinny") or name == "conv_listing":
         # the eager call is host-bound at this size: time the kernel in a graph
         out["ms_eager"] = ms
         out["ms"] = time_graph(run, 100, max(1, steps // 100), warmup)
@@ -378,6 +424,7 @@ KERNEL_SOURCES = {
     "gemv": ["gemv.hip"],
     "skinny": ["gemm_skinny.hip"],
     "attention": ["attention.hip"],
+    "conv": ["conv_implicit.hip"],
 }
 
 
@@ -388,6 +435,8 @@ def kernel_family(name):
         return "attention"
     if name.startswith("skinny"):
         return "skinny"
+    if name in CONV:
+        return "conv"
     return "gemm"
 
 
@@ -433,6 +482,8 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
         kernel_substr = "attn_fwd"
     elif name.startswith("skinny"):
         kernel_substr = "gemm_skinny"
+    elif name in CONV:
+        kernel_substr = "conv_implicit"
     f_k, nf = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", kernel_substr)
     w_k, nw = _counter_per_dispatch(write_csv, "WRITE_SIZE", kernel_substr)
     f_c, _ = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", copy_substr)
@@ -485,6 +536,8 @@ def cpu_baseline(name, r, target_s=20.0):
         return cpu_baseline_attention(name, r, target_s)
     if name in FULL_FORM:
         return cpu_baseline_full(name, r, target_s)
+    if name in CONV:
+        return cpu_baseline_conv(name, r, target_s)
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
     A, B, bvec, sa, sb = r["host"]
     if Z > 1:
@@ -552,6 +605,32 @@ def cpu_baseline_full(name, r, target_s=20.0):
             "cores": oracle.threads(), "kind": "oracle", "seconds": round(t, 2),
             "sample": f"{len(idx)} of {M} rows of the {describe(name)} product (fp64; time includes "
                       f"decoding the inputs)",
+            "sample_rel_fro_vs_gpu": err}
+
+
+def cpu_baseline_conv(name, r, target_s=20.0):
+    """The oracle's direct convolution on whole images (1, 2, 4, ... until
+    about target_s seconds), compared with the GPU's output for them."""
+    import oracle
+    c = CONV[name]
+    x, w, (sc, bi), _, _ = r["host"]
+    M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
+    n, t, out = 1, 0.0, None
+    while True:
+        t0 = time.perf_counter()
+        out = oracle.conv2d(fin, x[:n], w, c["pad"], sc, bi, True, c["pool"])
+        t = time.perf_counter() - t0
+        if t * 2 > target_s or n * 2 > c["N"]:
+            break
+        n *= 2
+    g = r["sets"][0][2][:n].float().cpu().numpy().astype(np.float64)
+    den = float(np.linalg.norm(out))
+    err = float(np.linalg.norm(g - out) / den) if den > 0 else float(np.linalg.norm(g - out))
+    per_img = gemm_flops(M // c["N"], N, K)
+    return {"value": round(per_img * n / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": round(t, 2),
+            "sample": f"{n} of {c['N']} images of the {describe(name)} workload (fp64 direct "
+                      f"convolution; time includes decoding)",
             "sample_rel_fro_vs_gpu": err}
 
 
@@ -641,6 +720,9 @@ def main(argv=None):
                    "input_copies_rotated": r["copies"]},
         "roofline": roof,
     }
+    if name in CONV:
+        line["metric"] = f"{describe(name)}: TFLOP/s (2 pixels K R S C / t)"
+        line["config"] = dict(workload=describe(name), **CONV[name], input_copies_rotated=r["copies"])
     if name in ATTENTION:
         line["config"] = {"workload": describe(name), "Nq": M, "Nk": N, "D": K, "batch_heads": Z,
                           "out": fout, "scale": "1/sqrt(D)", "input_copies_rotated": r["copies"]}
