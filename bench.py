@@ -716,7 +716,8 @@ def main(argv=None):
         "dtype": fin,
         "data": "synthetic",
         "config": {"workload": describe(name), "M": M, "N": N, "K": K, "batch": Z,
-                   "layout": "NT" if tb else "NN", "out": fout, "bias": bias,
+                   "layout": ("T" if FULL_FORM.get(name, {}).get("trans_a") else "N") + ("T" if tb else "N"),
+                   "out": fout, "bias": bias,
                    "input_copies_rotated": r["copies"]},
         "roofline": roof,
     }

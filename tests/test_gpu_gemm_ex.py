@@ -143,3 +143,43 @@ def test_beta_zero_does_not_read_c_and_empty_sum(tmm, monkeypatch):
     want = np.maximum(bvec.astype(np.float64)[None, :] - 2.0 * oracle.decode("f32", c0), 0.0)
     got = oracle.decode("f32", to_bits(C))
     np.testing.assert_allclose(got, want, rtol=2 ** -22, atol=0)
+
+
+# Transposed A on the 256x256 ring kernel: M and N ragged against the tile
+# (multiples of 8, as its 16-byte chunks need), both B layouts, both
+# epilogues (plain and full form), batched; a K that is not a multiple of 32
+# falls back to the any-layout kernel under the same forced name.
+RING_TA = [
+    # (M, N, K, fmt, out, tb, alpha, beta, relu, bias, batch)
+    (520, 776, 320, "bf16", "bf16", False, 1.5, 0.75, True, True, 1),
+    (264, 392, 96, "f16", "f32", False, 1.0, 0.0, False, False, 1),
+    (520, 776, 320, "bf16", "f32", True, 1.0, 0.0, False, True, 1),
+    (296, 136, 64, "f16", "f16", True, -0.5, 1.0, True, False, 1),
+    (300, 136, 64, "f16", "f16", True, -0.5, 1.0, True, False, 1),
+    (136, 264, 128, "bf16", "bf16", False, 1.0, 0.0, False, True, 3),
+    (200, 152, 104, "bf16", "bf16", False, 1.0, 0.5, False, True, 1),
+]
+
+
+@pytest.mark.parametrize("case", RING_TA, ids=[f"{c[0]}x{c[1]}x{c[2]}-{c[3]}-{c[4]}-{'T' if c[5] else 'N'}"
+                                               f"-b{c[10]}" for c in RING_TA])
+def test_transposed_a_ring(tmm, case, monkeypatch):
+    M, N, K, fmt, out, tb, alpha, beta, relu, bias, batch = case
+    monkeypatch.setenv("TMM_FORCE_TILE", "256x256r")
+    run_case(tmm, M, N, K, fmt, out, True, tb, alpha, beta, relu, bias, seed=1700 + M, batch=batch,
+             what=f"ring TA {case}")
+
+
+def test_transposed_a_ring_integer_exact(tmm, monkeypatch):
+    monkeypatch.setenv("TMM_FORCE_TILE", "256x256r")
+    for tb in (False, True):
+        run_case(tmm, 264, 520, 96, "bf16", "f32", True, tb, 2.0, -1.0, True, True, seed=1800,
+                 dist="int", what=f"int ring TA tb {tb}")
+
+
+def test_transposed_a_automatic_choice(tmm, monkeypatch):
+    """A weight-gradient shape large enough that the ring kernel is chosen
+    without forcing (2048 x 2048 outputs: 64 tiles of 256 x 256)."""
+    monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+    run_case(tmm, 2048, 2048, 128, "bf16", "f32", True, False, 1.0, 0.0, False, False, seed=1900,
+             what="auto TA 2048")

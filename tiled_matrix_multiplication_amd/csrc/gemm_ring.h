@@ -42,7 +42,12 @@
 //     32x32 accumulators.  NW = 4 (one wave per SIMD, 128x128 blocks as
 //     4x4: a third fewer LDS fragment reads per matrix instruction) also
 //     compiles but measured much slower and is not dispatched.  Tile order
-//     and edges as in gemm_mfma.h; the epilogue is store_tile_lds.
+//     and edges as in gemm_mfma.h; the epilogue is store_tile_lds;
+//   * TA: A stored K x M (the transposed operand of a weight gradient,
+//     X^T . dY), 16-bit inputs.  Its stage is k-rows of BM elements placed
+//     like the NN B stage, and its fragments come from the same transposing
+//     reads (the instruction's A and B fragments share one lane layout), so
+//     a transposed A costs LDS read rate, not a transposing copy.
 #pragma once
 
 #include "gemm_mfma.h"
@@ -97,7 +102,7 @@ __device__ __forceinline__ int nn_swz(int row) {
   return E == 2 ? 4 * (row & 3) : (row & 7);
 }
 
-template <int AB, int CT, bool NT, int NW, bool FULL>
+template <int AB, int CT, bool NT, int NW, bool FULL, bool TA = false>
 __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   constexpr int BM = 256, BN = 256;
   constexpr int E = FmtBytes<AB>::value;
@@ -105,16 +110,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   constexpr int BK = kRingRowBytes / E;            // K per step
   constexpr int WGN = NW / 2, WTM = BM / 2, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;      // 4 x 2 accumulators per wave
-  constexpr int A_BYTES = BM * kRingRowBytes;      // 16 KiB
+  constexpr int A_BYTES = BM * kRingRowBytes;      // 16 KiB (TA: BK k-rows x BM*E B)
   constexpr int B_BYTES = BN * kRingRowBytes;      // 16 KiB (NT: BN rows x 64 B; NN: BK rows x BN*E B)
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int NB_ROW = BN * E;                   // NN: bytes of one k-row of the B stage
   constexpr int CPR = NB_ROW / 16, RPI = 64 / CPR; // NN: chunks per k-row, k-rows per load
+  constexpr int NA_ROW = BM * E;                   // TA: bytes of one k-row of the A stage
+  constexpr int CPR_A = NA_ROW / 16, RPI_A = 64 / CPR_A;
   constexpr int LA = A_BYTES / 1024 / NW;          // direct loads per wave per step (A)
   constexpr int LB = B_BYTES / 1024 / NW;          // (B)
   constexpr int LPS = LA + LB;
   static_assert(E == 2 || E == 1, "ring path: 16-bit and fp8 inputs (fp32 uses the two-stage kernel)");
   static_assert((NW == 8 || NW == 4) && LA == 16 / NW && LB == 16 / NW, "ring geometry");
+  static_assert(!TA || E == 2, "transposed A: 16-bit inputs");
 
   __shared__ __attribute__((aligned(16))) char lds[kRingStages * STAGE];
 
@@ -142,11 +150,25 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   // lane L lands at row L/4, position L%4 and loads logical chunk
   // (L%4) ^ swz64(row).
   uint32_t a_off[LA], b_off[LB];
+  if constexpr (TA) {
+    // A stored K x M: k-rows of NA_ROW bytes, placed like the NN B stage
+    // (chunk c of k-row r at position c ^ nn_swz(r)); a chunk wholly past M
+    // (the host ensures M*E % 16 == 0) reads chunk 0 of the tile instead.
 #pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int row = wave * (BM / NW) + i * 16 + (lane >> 2);
-    const int64_t r = min64(m0 + row, M - 1);
-    a_off[i] = (uint32_t)(r * p.lda * E + (((lane & 3) ^ swz64(row)) << 4));
+    for (int i = 0; i < LA; ++i) {
+      const int row = wave * (BK / NW) + i * RPI_A + lane / CPR_A;
+      const int c = (lane % CPR_A) ^ nn_swz<E>(row);
+      const int64_t col = m0 + (int64_t)c * (16 / E);
+      const int64_t ccol = col < M ? col : m0;
+      a_off[i] = (uint32_t)(((int64_t)row * p.lda + ccol) * E);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int row = wave * (BM / NW) + i * 16 + (lane >> 2);
+      const int64_t r = min64(m0 + row, M - 1);
+      a_off[i] = (uint32_t)(r * p.lda * E + (((lane & 3) ^ swz64(row)) << 4));
+    }
   }
   if constexpr (NT) {
 #pragma unroll
@@ -171,15 +193,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
     }
   }
   const int64_t kstep_b = NT ? (int64_t)kRingRowBytes : (int64_t)BK * p.ldb * E;
+  const int64_t kstep_a = TA ? (int64_t)BK * p.lda * E : (int64_t)kRingRowBytes;
 
   const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int64_t kt, int stage) __attribute__((always_inline)) {
     const uint32_t la = lds0 + (uint32_t)(stage * STAGE);
-    const char *ak = A + kt * kRingRowBytes;
+    const char *ak = A + kt * kstep_a;
     const char *bk = B + kt * kstep_b;
 #pragma unroll
-    for (int i = 0; i < LA; ++i)
-      dma16(ak + a_off[i], la + (wave * (BM / NW) + i * 16) * kRingRowBytes);
+    for (int i = 0; i < LA; ++i) {
+      if constexpr (TA)
+        dma16(ak + a_off[i], la + (wave * (BK / NW) + i * RPI_A) * NA_ROW);
+      else
+        dma16(ak + a_off[i], la + (wave * (BM / NW) + i * 16) * kRingRowBytes);
+    }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       if constexpr (NT)
@@ -202,6 +229,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   const int G = lane >> 4, q = lane & 15;
   const int tr_row0 = 8 * (G >> 1) + (q >> 2);       // + 16 s + 4 h
   const int tr_col0 = wn * WTN + 16 * (G & 1) + 4 * (q & 3);  // + 32 j (elements)
+  const int tr_acol0 = wm * WTM + 16 * (G & 1) + 4 * (q & 3); // TA: + 32 i
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -248,14 +276,31 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
   // 16-lane group points at k-row (piece base) + q/2, columns (block) +
   // 16 (G%2) + 8 (q%2) .. +7).  B, NN, 16-bit: four 16-bit transposing
   // reads per block, piece t = 2 s + h holding k 16 s + 8 g + 4 h .. +3.
+  // A, TA: the same four transposing reads per block as B, NN, since the
+  // instruction's A and B fragments have one layout (lane l: row / column
+  // l % 32, k 8 (l / 32) .. +7).
   constexpr int RBS = FN * (NT ? 2 : 4);
-  constexpr int NRS = RBS + 2 * FM;
+  constexpr int NRS = RBS + (TA ? 4 : 2) * FM;
   i32x2 pcs[FN][4];
+  i32x2 pca[FM][4];
   auto read_r = [&](int stage, FragA &na, FragB &nb, int r) __attribute__((always_inline)) {
     const char *base = lds + stage * STAGE;
     if (r >= RBS) {
-      const int i = (r - RBS) >> 1, s2 = (r - RBS) & 1;
-      na[s2][i] = *(const i32x4 *)(base + a_frag + i * 32 * kRingRowBytes + a_ch[s2]);
+      if constexpr (TA) {
+        const int i = (r - RBS) >> 2, t = (r - RBS) & 3;
+        const int row = 16 * (t >> 1) + 4 * (t & 1) + tr_row0;
+        const int col = tr_acol0 + 32 * i;
+        const int chunk = (col * E) >> 4, within = (col * E) & 15;
+        pca[i][t] = __builtin_bit_cast(
+            i32x2, lds_read_tr16(base + row * NA_ROW + ((chunk ^ nn_swz<E>(row)) << 4) + within));
+        if (t & 1) {
+          const int s2 = t >> 1;
+          na[s2][i] = i32x4{pca[i][t - 1][0], pca[i][t - 1][1], pca[i][t][0], pca[i][t][1]};
+        }
+      } else {
+        const int i = (r - RBS) >> 1, s2 = (r - RBS) & 1;
+        na[s2][i] = *(const i32x4 *)(base + a_frag + i * 32 * kRingRowBytes + a_ch[s2]);
+      }
     } else if constexpr (NT) {
       const int j = r >> 1, s2 = r & 1;
       nb[s2][j] = *(const i32x4 *)(base + A_BYTES + (wn * WTN + j * 32 + l32) * kRingRowBytes + a_ch[s2]);
@@ -352,6 +397,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(GemmParams p) {
     store_tile_lds<CT, FM, FN>(acc, lds + wave * 32 * stage_pitch<CT, WTN>(), C, p.ldc, M, N,
                                m0 + wm * WTM, n0 + wn * WTN, p.bias, p.scale, lane);
   }
+}
+
+// A stored K x M (16-bit inputs); the host ensures M*E % 16 == 0, 16-byte
+// aligned rows of A and B and K % 32 == 0.
+template <int AB, int CT, bool NT>
+hipError_t launch_ring_ta(const GemmParams &p, hipStream_t stream) {
+  const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
+  if (p.beta != 0.f || p.act != 0)
+    hipLaunchKernelGGL((gemm_ring_kernel<AB, CT, NT, 8, true, true>), dim3((unsigned)tiles), dim3(512), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((gemm_ring_kernel<AB, CT, NT, 8, false, true>), dim3((unsigned)tiles), dim3(512), 0,
+                       stream, p);
+  return hipGetLastError();
 }
 
 template <int AB, int CT, bool NT, int NW>

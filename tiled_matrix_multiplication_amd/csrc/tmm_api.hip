@@ -107,7 +107,8 @@ int cu_count() {
 // tests ("256x256s2": 256x256 tiles on the two-stage kernel only; "256x256r":
 // on the ring kernel wherever it applies, K-contiguous B included; "skinny":
 // the skinny-M kernel wherever it applies, any M; "generic": the any-layout
-// kernel for 16-bit inputs).
+// kernel for 16-bit inputs; with a transposed A, "256x256" and "256x256r"
+// pick the ring kernel wherever it applies).
 // Read on every call so that a test can switch it; anything else leaves the
 // choice to pick_tile.
 int forced_tile() {
@@ -190,6 +191,23 @@ tmm::Tile pick_tile(int64_t M, int64_t N, int64_t batch, int ab) {
   return best;
 }
 
+// Transposed A: the 256x256 ring kernel or the 64x64 any-layout kernel,
+// by the same rounds-times-tile-work estimate as pick_tile (the any-layout
+// kernel measured at about an eighth of the ring kernel's rate).  A forced
+// "generic" takes the latter, a forced 256x256 shape the former.
+bool use_ring_ta(int64_t M, int64_t N, int64_t batch) {
+  const int f = forced_tile();
+  if (f == tmm::kTile256x256 || f == tmm::kTile256x256r) return true;
+  const char *s = getenv("TMM_FORCE_TILE");
+  if (s && !strcmp(s, "generic")) return false;
+  const int cus = cu_count();
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256) * batch;
+  const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64) * batch;
+  const double ring = (double)((t256 + cus - 1) / cus) * 256.0 * 256.0;
+  const double gen = (double)((t64 + cus - 1) / cus) * 64.0 * 64.0 * 8.0;
+  return ring <= gen;
+}
+
 hipError_t dispatch_gemm(int ab, int c, bool trans_b, tmm::Tile tile, bool vec,
                          const tmm::GemmParams &p, hipStream_t s) {
   switch (ab) {
@@ -228,7 +246,13 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
     const int e = elem_bytes(ab);
     const bool va = aligned(A, 16) && (lda * e) % 16 == 0 && (batch == 1 || (sA * e) % 16 == 0);
     const bool vb = aligned(B, 16) && (ldb * e) % 16 == 0 && (batch == 1 || (sB * e) % 16 == 0);
-    err = tmm::launch_gemm_generic((Fmt)ab, (Fmt)c, true, trans_b != 0, va, vb, p, stream);
+    // the ring kernel reads whole 16-byte chunks of A's (and an NN B's)
+    // k-rows and takes whole 32-element K-steps
+    const bool ring_ok = va && vb && (M * e) % 16 == 0 && (trans_b || (N * e) % 16 == 0) && K % 32 == 0;
+    if (ring_ok && use_ring_ta(M, N, batch))
+      err = tmm::launch_gemm_ring_ta((Fmt)ab, (Fmt)c, trans_b != 0, p, stream);
+    else
+      err = tmm::launch_gemm_generic((Fmt)ab, (Fmt)c, true, trans_b != 0, va, vb, p, stream);
   } else if (M == 1 && batch == 1 && trans_b && ab != TMM_F8E4M3 && plain &&
              forced_tile() != tmm::kTileSkinny) {
     // y = W . x with W = B (N x K): the memory-bound matrix-vector path.

@@ -71,6 +71,11 @@ hipError_t launch_gemm_skinny(Fmt ab, Fmt c, int bm, int bn, bool vec_c, const G
 hipError_t launch_gemm_generic(Fmt ab, Fmt c, bool trans_a, bool trans_b, bool vec_a, bool vec_b,
                                const GemmParams &p, hipStream_t stream);
 
+// 256 x 256 ring kernel with A stored K x M (16-bit inputs): every row of A
+// and B 16-byte aligned, M*E and (for an N-contiguous B) N*E multiples of
+// 16, K a multiple of 32.
+hipError_t launch_gemm_ring_ta(Fmt ab, Fmt c, bool trans_b, const GemmParams &p, hipStream_t stream);
+
 // C = act(bias + beta * old C) (bias, beta default none) for the K == 0
 // empty sum.
 hipError_t launch_fill(Fmt c, const GemmParams &p, hipStream_t stream);
