@@ -14,10 +14,13 @@
 //     in contiguous runs, so the row panels that share a weight panel run
 //     together on one XCD and the weight comes from HBM once;
 //   * the NW waves of a workgroup (16 for the small tiles, 8 for the wide
-//     ones) split K: wave w takes the 32-element K steps w, w + NW, ...
+//     ones) split K: wave w takes the 64-element K steps w, w + NW, ...
 //     (together they read contiguous row pieces), so the weight panel
 //     streams through all of them at once with 48-128 KiB of loads in
-//     flight per CU;
+//     flight per CU.  A step is two 32-element pieces, one matrix
+//     instruction each, loaded back to back, so the 64-byte pieces of a row
+//     that one wave requests make whole 128-byte lines (one piece per step
+//     measured 9-12 % slower at M = 4 ... 256);
 //   * both operands are K-contiguous rows, which is what the MFMA operands
 //     want: 16-byte global loads go straight into registers (no LDS, no
 //     transposes), P steps ahead of their use;
@@ -30,7 +33,8 @@
 //     stores (in the full form also + beta * old C and ReLU before the
 //     rounding).
 // Rows past M (columns past N) read the last valid row and are not stored;
-// a K tail (K % 32) is read element by element with zero fill.
+// a K tail (K % 64) is read element by element with zero fill, one 32-wide
+// piece at a time.
 #include <stdint.h>
 
 #include "tmm_internal.h"
@@ -90,7 +94,7 @@ __device__ __forceinline__ i32x4 load_tail(const uint16_t *row, int64_t k, int64
   return v;
 }
 
-template <int AB, int CT, int BM, int BN, int P, int NW>
+template <int AB, int CT, int BM, int BN, int P, int NW, int KP>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(GemmParams p, int64_t tiles_m,
                                                                   int64_t tiles_n, int vec_c) {
   constexpr int kWaves = NW;
@@ -134,21 +138,31 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(GemmParams p, i
 
   // Full K steps of this wave: s = wave + NW i, i < cnt.  Ring of P steps of
   // fragments; step i sits in slot i % P.
-  const int64_t nfull = K / kKS;
+  // A wave's step is KP consecutive 32-element pieces: with KP = 2 the two
+  // 64-byte pieces of each row it loads make one whole 128-byte line.
+  constexpr int KSTEP = kKS * KP;
+  const int64_t nfull = K / KSTEP;
   const int64_t cnt = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
-  i32x4 fa[P][FM], fb[P][FN];
+  i32x4 fa[P][KP][FM], fb[P][KP][FN];
   auto load = [&](int64_t i, int slot) __attribute__((always_inline)) {
-    const int64_t k = (wave + kWaves * i) * kKS + 8 * kq;
+    const int64_t k = (wave + kWaves * i) * KSTEP + 8 * kq;
 #pragma unroll
-    for (int f = 0; f < FM; ++f) fa[slot][f] = *(const i32x4 *)(arow[f] + k);
+    for (int h = 0; h < KP; ++h) {
 #pragma unroll
-    for (int f = 0; f < FN; ++f) fb[slot][f] = *(const i32x4 *)(brow[f] + k);
+      for (int f = 0; f < FM; ++f) fa[slot][h][f] = *(const i32x4 *)(arow[f] + k + h * kKS);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) fb[slot][h][f] = *(const i32x4 *)(brow[f] + k + h * kKS);
+    }
   };
-  auto compute = [&](const i32x4 (&a)[FM], const i32x4 (&b)[FN]) __attribute__((always_inline)) {
+  auto compute1 = [&](const i32x4 (&a)[FM], const i32x4 (&b)[FN]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = mma<AB>(a[i], b[j], acc[i][j]);
+  };
+  auto compute = [&](const i32x4 (&a)[KP][FM], const i32x4 (&b)[KP][FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < KP; ++h) compute1(a[h], b[h]);
   };
 
 #pragma unroll
@@ -166,15 +180,18 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(GemmParams p, i
   for (int q = 0; q < P; ++q)
     if (i + q < cnt) compute(fa[q], fb[q]);
 
-  // K tail: one partial step, owned by the wave whose turn it is.
-  if (K % kKS != 0 && wave == (int)(nfull % kWaves)) {
-    const int64_t k = nfull * kKS + 8 * kq;
-    i32x4 a[FM], b[FN];
+  // K tail past the whole steps: up to KP partial pieces, owned by the wave
+  // whose turn it is.
+  if (K % KSTEP != 0 && wave == (int)(nfull % kWaves)) {
+    for (int64_t k0 = nfull * KSTEP; k0 < K; k0 += kKS) {
+      const int64_t k = k0 + 8 * kq;
+      i32x4 a[FM], b[FN];
 #pragma unroll
-    for (int f = 0; f < FM; ++f) a[f] = load_tail(arow[f], k, K);
+      for (int f = 0; f < FM; ++f) a[f] = load_tail(arow[f], k, K);
 #pragma unroll
-    for (int f = 0; f < FN; ++f) b[f] = load_tail(brow[f], k, K);
-    compute(a, b);
+      for (int f = 0; f < FN; ++f) b[f] = load_tail(brow[f], k, K);
+      compute1(a, b);
+    }
   }
 
   // Tree sum of the partial tiles: at half-width h, waves h .. 2h-1 store
@@ -265,33 +282,33 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(GemmParams p, i
   }
 }
 
-template <int AB, int CT, int BM, int BN, int P, int NW>
+template <int AB, int CT, int BM, int BN, int P, int NW, int KP = 2>
 hipError_t launch_one(const GemmParams &p, int vec_c, hipStream_t stream) {
   const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int64_t blocks = tiles_m * tiles_n * p.batch;
-  hipLaunchKernelGGL((gemm_skinny_kernel<AB, CT, BM, BN, P, NW>), dim3((unsigned)blocks), dim3(64 * NW),
+  hipLaunchKernelGGL((gemm_skinny_kernel<AB, CT, BM, BN, P, NW, KP>), dim3((unsigned)blocks), dim3(64 * NW),
                      0, stream, p, tiles_m, tiles_n, vec_c);
   return hipGetLastError();
 }
 
-// Prefetch depth P and waves NW per tile: registers within the 128 (NW =
-// 16) or 256 (NW = 8) a wave may hold, 48-128 KiB of B loads in flight per
-// workgroup.
+// Prefetch depth P (in two-piece steps) and waves NW per tile: registers
+// within the 128 (NW = 16) or 256 (NW = 8) a wave may hold without
+// spilling, 48-128 KiB of B loads in flight per workgroup.
 template <int AB, int CT>
 hipError_t launch_typed(int bm, int bn, const GemmParams &p, int vec_c, hipStream_t s) {
   if (bm == 16) {
-    if (bn == 16) return launch_one<AB, CT, 16, 16, 8, 16>(p, vec_c, s);
-    if (bn == 32) return launch_one<AB, CT, 16, 32, 5, 16>(p, vec_c, s);
-    return launch_one<AB, CT, 16, 64, 3, 16>(p, vec_c, s);
+    if (bn == 16) return launch_one<AB, CT, 16, 16, 6, 16>(p, vec_c, s);
+    if (bn == 32) return launch_one<AB, CT, 16, 32, 3, 16>(p, vec_c, s);
+    return launch_one<AB, CT, 16, 64, 1, 16>(p, vec_c, s);
   }
   if (bm == 32) {
-    if (bn == 16) return launch_one<AB, CT, 32, 16, 5, 16>(p, vec_c, s);
-    if (bn == 32) return launch_one<AB, CT, 32, 32, 4, 16>(p, vec_c, s);
-    return launch_one<AB, CT, 32, 64, 3, 8>(p, vec_c, s);
+    if (bn == 16) return launch_one<AB, CT, 32, 16, 3, 16>(p, vec_c, s);
+    if (bn == 32) return launch_one<AB, CT, 32, 32, 2, 16>(p, vec_c, s);
+    return launch_one<AB, CT, 32, 64, 2, 8>(p, vec_c, s);
   }
-  if (bn == 16) return launch_one<AB, CT, 64, 16, 3, 16>(p, vec_c, s);
-  if (bn == 32) return launch_one<AB, CT, 64, 32, 3, 8>(p, vec_c, s);
-  return launch_one<AB, CT, 64, 64, 2, 8>(p, vec_c, s);
+  if (bn == 16) return launch_one<AB, CT, 64, 16, 1, 16>(p, vec_c, s);
+  if (bn == 32) return launch_one<AB, CT, 64, 32, 2, 8>(p, vec_c, s);
+  return launch_one<AB, CT, 64, 64, 1, 8>(p, vec_c, s);
 }
 
 }  // namespace
