@@ -212,6 +212,7 @@ def test_softmax_weights_stay_in_value_hull(tmm):
     (4096, 4096, "bf16", "bf16", "normal", True),
     (4096, 4096, "bf16", "f32", "normal", True),
     (1000, 4096, "bf16", "bf16", "int", True),
+    (96, 8192, "bf16", "bf16", "normal", True),       # two unchecked passes per row
     (777, 777, "bf16", "f32", "normal", False),       # element path (rows not 16-byte aligned)
     (513, 1032, "f16", "f16", "normal", True),
     (300, 2048, "f32", "f32", "normal", True),
