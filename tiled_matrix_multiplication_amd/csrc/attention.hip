@@ -92,12 +92,18 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 // LDS swizzles.  K tile: the score fragments read 32 consecutive rows at one
-// chunk, so chunk c of row r sits at c ^ (r mod CPR).  V tile: a transposing
-// read takes 4 consecutive rows x 2 chunks, so chunk c of row r sits at
-// c ^ 2 (r mod 4).
+// chunk, so chunk c of row r sits at c ^ (r mod CPR).  V tile: the
+// transposing reads of 32 lanes take 4 consecutive rows x 4 chunks (two
+// 16-lane halves, 2 chunks each).  With 256-byte rows (D = 128) every row
+// spans all 64 banks, so the 4 rows must land on 4 disjoint 64-byte bank
+// groups: chunk c of row r sits at c ^ 4 (r mod 4) (c ^ 2 (r mod 4) gave
+// two rows the same banks: SQ_LDS_BANK_CONFLICT was 32 % of
+// SQ_LDS_IDX_ACTIVE).  With 128-byte rows (D = 64) odd rows already sit on
+// the other half of the banks and c ^ 2 (r mod 4) separates the rest.
 template <int CPR>
 __device__ __forceinline__ int kswz(int row) { return row & (CPR - 1); }
-__device__ __forceinline__ int vswz(int row) { return 2 * (row & 3); }
+template <int CPR>
+__device__ __forceinline__ int vswz(int row) { return (CPR >= 16 ? 4 : 2) * (row & 3); }
 
 // Two waves per SIMD (two workgroups per CU, 64 KiB of LDS each): at most
 // 256 registers per lane.
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_fwd_kernel(AttnParams p) 
   for (int i = 0; i < LPT; ++i) {
     const int row = (wave * LPT + i) * RPI + lane / CPR;
     koff[i] = (uint32_t)(row * p.ldk * E) + ((pos ^ kswz<CPR>(row)) << 4);
-    voff[i] = (uint32_t)(row * p.ldv * E) + ((pos ^ vswz(row)) << 4);
+    voff[i] = (uint32_t)(row * p.ldv * E) + ((pos ^ vswz<CPR>(row)) << 4);
   }
   auto issue = [&](int64_t kb, int st) __attribute__((always_inline)) {
     const char *kbase = Kz + kb * kBK * p.ldk * E;
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_fwd_kernel(AttnParams p) 
         const int row = (wave * LPT + i) * RPI + lane / CPR;
         const int64_t r = row < left ? row : left - 1;
         ko = (uint32_t)(r * p.ldk * E) + ((pos ^ kswz<CPR>(row)) << 4);
-        vo = (uint32_t)(r * p.ldv * E) + ((pos ^ vswz(row)) << 4);
+        vo = (uint32_t)(r * p.ldv * E) + ((pos ^ vswz<CPR>(row)) << 4);
       }
       dma16(kbase, ko, dst);
       dma16(vbase, vo, dst + TILE);
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attn_fwd_kernel(AttnParams p) 
             const int row = base + 8 * t + 4 * (G >> 1) + (q16 >> 2);
             const int col = 32 * b + 16 * (G & 1) + 4 * (q16 & 3);   // element column
             const int chunk = col >> 3, within = (col & 7) * E;
-            tr[t] = lds_read_tr16(Vt + row * RB + ((chunk ^ vswz(row)) << 4) + within);
+            tr[t] = lds_read_tr16(Vt + row * RB + ((chunk ^ vswz<CPR>(row)) << 4) + within);
           }
           const i32x2 t0 = __builtin_bit_cast(i32x2, tr[0]), t1 = __builtin_bit_cast(i32x2, tr[1]);
           const i32x4 vf = {t0[0], t0[1], t1[0], t1[1]};

@@ -95,11 +95,15 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const char *p) {
 }
 
 // NN B stage: 16-byte chunk c of k-row r sits at position c ^ nn_swz(r).
-// The transposing reads take 4 (16-bit) or 8 (8-bit) consecutive k-rows at
-// one chunk; the XOR puts them on distinct bank groups.
+// An 8-byte transposing read is served 32 lanes at a time (256 bytes, all
+// 64 banks): 16-bit, 4 consecutive k-rows x 4 chunks; 8-bit, 8 consecutive
+// k-rows x 2 adjacent chunks (an even one and the next).  The XOR puts
+// those on 16 distinct chunk positions.  (For 8-bit, c ^ (r mod 8) mapped
+// rows 2i and 2i+1 onto the same pair of positions: SQ_LDS_BANK_CONFLICT
+// was 25 % of SQ_LDS_IDX_ACTIVE.)
 template <int E>
 __device__ __forceinline__ int nn_swz(int row) {
-  return E == 2 ? 4 * (row & 3) : (row & 7);
+  return E == 2 ? 4 * (row & 3) : 2 * (row & 7);
 }
 
 template <int AB, int CT, bool NT, int NW, bool FULL, bool TA = false>
