@@ -162,11 +162,26 @@ __device__ __forceinline__ uint32_t out_bits(float v) {
   else return f32_to_f16_rne(v);
 }
 
-// Row pitch (bytes) of a wave's epilogue staging area for WT columns: the
-// row plus 32 bytes, so rows r and r + 4 (one store instruction of the
-// accumulator layout) start 32 banks apart.
+// Row pitch (bytes) of a wave's epilogue staging area for WT columns.
+// fp32: the row plus 32 bytes, so rows r and r + 4 (one store instruction
+// of the accumulator layout) start 32 banks apart.  16-bit rows of 8 or more
+// 16-byte pieces: no padding, and piece p of row r sits at p ^ stage_swz(r)
+// instead -- rows r and r + 4 (one write instruction) put their 4 pieces
+// in disjoint halves of the row, and each 16 lanes of a read-back take 256
+// contiguous bytes (two 128-byte rows or one 256-byte row).  The padded
+// 16-bit pitch left two rows of one read on the same banks:
+// SQ_LDS_BANK_CONFLICT was 20-25 % of SQ_LDS_IDX_ACTIVE where this
+// epilogue weighs (batched 2048 x 2048 x 128 fp16 out).
 template <int CT, int WT>
-constexpr int stage_pitch() { return WT * FmtBytes<CT>::value + 32; }
+constexpr bool stage_swizzled() { return FmtBytes<CT>::value == 2 && WT * 2 / 16 >= 8; }
+template <int CT, int WT>
+constexpr int stage_pitch() {
+  return stage_swizzled<CT, WT>() ? WT * 2 : WT * FmtBytes<CT>::value + 32;
+}
+template <int CT, int WT>
+__device__ __forceinline__ int stage_swz(int row) {
+  return stage_swizzled<CT, WT>() ? 4 * ((row >> 2) & 1) : 0;
+}
 
 // Epilogue through LDS.  For each 32-row band i of the wave's block, the
 // accumulators go to the wave's own LDS area `st` (32 rows, stage_pitch
@@ -207,7 +222,8 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[FM][FN], char
       for (int r = 0; r < 16; ++r) {
         const int row = 8 * (r >> 2) + 4 * g + (r & 3);
         const uint32_t b = out_bits<CT>(acc[i][j][r] * scale + bv[j]);
-        char *d = st + row * P + (j * 32 + l32) * CE;
+        const int byte = (j * 32 + l32) * CE;
+        char *d = st + row * P + ((((byte >> 4) ^ stage_swz<CT, WT>(row)) << 4) | (byte & 15));
         if constexpr (CE == 4) *(uint32_t *)d = b;
         else *(uint16_t *)d = (uint16_t)b;
       }
@@ -218,7 +234,7 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[FM][FN], char
     for (int t = 0; t < NRD; ++t) {
       const int c = t * 64 + lane;
       const int row = c / CPR, pc = c % CPR;
-      const i32x4 v = *(const i32x4 *)(st + row * P + pc * 16);
+      const i32x4 v = *(const i32x4 *)(st + row * P + ((pc ^ stage_swz<CT, WT>(row)) << 4));
       const int64_t grow = row0 + i * 32 + row;
       const int64_t gcol = col0 + (int64_t)pc * EPC;
       if (grow >= M || gcol >= N) continue;
