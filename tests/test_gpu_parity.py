@@ -124,6 +124,59 @@ def test_batched_parity_and_batch_identity(tmm, trans_b):
         assert torch.equal(one, C[z]), f"batch slice {z} differs from the single call"
 
 
+def _batched_nt(Z, M, N, K, fmt, seed):
+    A = syn.to_bits(syn.normal((Z, M, K), seed), fmt)
+    B = syn.to_bits(syn.normal((Z, N, K), seed + 1), fmt)
+    return A, B
+
+
+def _run_batched_nt(tmm, A, B, fmt, tile, monkeypatch):
+    if tile is None:
+        monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+    else:
+        monkeypatch.setenv("TMM_FORCE_TILE", tile)
+    Z, M, K = A.shape
+    N = B.shape[1]
+    C = torch.full((Z, M, N), float("nan"), dtype=TORCH_DT[fmt], device=DEV)
+    tmm.tmm_gemm_strided_batched(on_gpu(A, fmt), on_gpu(B, fmt), C, trans_b=True)
+    torch.cuda.synchronize()
+    return C
+
+
+@pytest.mark.parametrize("Z,M,N,K,fmt", [
+    (3, 512, 256, 128, "f16"),    # 6 tiles, 8 workgroups (two idle)
+    (2, 256, 768, 64, "bf16"),    # K = 64: 128-byte operand rows
+    (9, 512, 512, 64, "f16"),     # 36 tiles on 32 workgroups: four walk two
+    (5, 768, 512, 128, "bf16"),   # 30 tiles on 24 workgroups, across batch entries
+], ids=["f16-K128-6tiles", "bf16-K64", "f16-K64-walk", "bf16-K128-walk"])
+def test_short_k_kernel(tmm, monkeypatch, Z, M, N, K, fmt):
+    """The persistent short-K kernel (forced): every batch entry against the
+    oracle, and bit for bit against the two-stage kernel (same matrix
+    instructions in the same K order)."""
+    A, B = _batched_nt(Z, M, N, K, fmt, 61 + K)
+    C = _run_batched_nt(tmm, A, B, fmt, "shortk", monkeypatch)
+    for z in range(Z):
+        o, T = oracle.gemm(fmt, A[z], B[z], trans_b=True, want_abs=True)
+        check(C[z], o, T, K, what=f"short-K batch {z}")
+    ref = _run_batched_nt(tmm, A, B, fmt, "256x256s2", monkeypatch)
+    assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), "short-K and two-stage kernels differ"
+
+
+def test_attention_scores_shape_takes_short_k(tmm, monkeypatch):
+    """Short K over many whole tiles (64 problems x 16 tiles, K = 128) is what
+    the dispatch sends to the short-K kernel without forcing: the result
+    equals the two-stage kernel's bit for bit, and sampled problems match the
+    oracle."""
+    Z, M, N, K = 64, 1024, 1024, 128
+    A, B = _batched_nt(Z, M, N, K, "f16", 81)
+    C = _run_batched_nt(tmm, A, B, "f16", None, monkeypatch)
+    for z in (0, 37, 63):
+        o, T = oracle.gemm("f16", A[z], B[z], trans_b=True, want_abs=True)
+        check(C[z], o, T, K, what=f"scores batch {z}")
+    ref = _run_batched_nt(tmm, A, B, "f16", "256x256s2", monkeypatch)
+    assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), "short-K and two-stage kernels differ"
+
+
 def test_batched_broadcast_operand(tmm):
     """Stride 0 for B: one B for every problem."""
     Z, M, N, K = 4, 128, 192, 64

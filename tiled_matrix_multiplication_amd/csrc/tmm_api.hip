@@ -9,6 +9,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "tmm.h"
@@ -103,12 +104,13 @@ int cu_count() {
 }
 
 // TMM_FORCE_TILE = "256x256" | "256x128" | "128x128" | "256x256w4" | "256x256s2" |
-// "256x256r" | "skinny" | "generic" pins the tile shape for measurements and tile-by-tile
+// "256x256r" | "skinny" | "generic" | "shortk" pins the tile shape for measurements and tile-by-tile
 // tests ("256x256s2": 256x256 tiles on the two-stage kernel only; "256x256r":
 // on the ring kernel wherever it applies, K-contiguous B included; "skinny":
 // the skinny-M kernel wherever it applies, any M; "generic": the any-layout
-// kernel for 16-bit inputs; with a transposed A, "256x256" and "256x256r"
-// pick the ring kernel wherever it applies).
+// kernel for 16-bit inputs; "shortk": the persistent short-K kernel
+// wherever it applies, any tile count; with a transposed A, "256x256" and
+// "256x256r" pick the ring kernel wherever it applies).
 // Read on every call so that a test can switch it; anything else leaves the
 // choice to pick_tile.
 int forced_tile() {
@@ -122,6 +124,11 @@ int forced_tile() {
   if (!strcmp(s, "256x256r")) return tmm::kTile256x256r;
   if (!strcmp(s, "skinny")) return tmm::kTileSkinny;
   return -1;
+}
+
+bool forced_short_k() {
+  const char *s = getenv("TMM_FORCE_TILE");
+  return s && !strcmp(s, "shortk");
 }
 
 // Largest M for which the skinny-M kernel is chosen automatically.
@@ -216,6 +223,22 @@ bool use_ring_ta(int64_t M, int64_t N, int64_t batch) {
   return ring <= gen;
 }
 
+// The persistent short-K kernel (gemm_short_k.hip): C = A . B^T, 16-bit in
+// and out of one type, K = 64 or 128, whole 256x256 tiles, no bias, plain
+// form, aligned rows and C.  Chosen automatically with at least four tiles
+// per CU (a write-bound product: batched 2048 x 2048 x 128 fp16, the
+// attention scores, 272 us on the two-stage kernel); "shortk" forces it.
+bool short_k_ok(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const void *C,
+                int64_t ldc, int64_t sC, int64_t batch, const float *bias, bool plain, bool vec) {
+  const int f = forced_tile();
+  if (f >= 0 && !forced_short_k()) return false;
+  if (!vec || !trans_b || !plain || bias || c != ab || (ab != TMM_BF16 && ab != TMM_F16)) return false;
+  if ((K != 64 && K != 128) || M % 256 != 0 || N % 256 != 0) return false;
+  if (!aligned(C, 16) || (ldc * 2) % 16 != 0 || (batch > 1 && (sC * 2) % 16 != 0)) return false;
+  if (forced_short_k()) return true;
+  return (M / 256) * (N / 256) * batch >= 4 * (int64_t)cu_count();
+}
+
 hipError_t dispatch_gemm(int ab, int c, bool trans_b, tmm::Tile tile, bool vec,
                          const tmm::GemmParams &p, hipStream_t s) {
   switch (ab) {
@@ -290,6 +313,11 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
       const bool va = aligned(A, 16) && (lda * e) % 16 == 0 && (batch == 1 || (sA * e) % 16 == 0);
       const bool vb = aligned(B, 16) && (ldb * e) % 16 == 0 && (batch == 1 || (sB * e) % 16 == 0);
       err = tmm::launch_gemm_generic((Fmt)ab, (Fmt)c, false, trans_b != 0, va, vb, p, stream);
+    } else if (short_k_ok(M, N, K, ab, c, trans_b, C, ldc, sC, batch, bias, plain, vec)) {
+      const int64_t total = (M / 256) * (N / 256) * batch;
+      const int64_t cus = cu_count();
+      const unsigned grid = (unsigned)std::max<int64_t>(8, std::min<int64_t>(total, cus) / 8 * 8);
+      err = tmm::launch_gemm_short_k((Fmt)ab, p, grid, stream);
     } else if (skinny_ok && (f == tmm::kTileSkinny || (f < 0 && M <= kSkinnyMaxM))) {
       int bm, bn;
       pick_skinny(M, N, batch, &bm, &bn);

@@ -76,6 +76,13 @@ hipError_t launch_gemm_generic(Fmt ab, Fmt c, bool trans_a, bool trans_b, bool v
 // 16, K a multiple of 32.
 hipError_t launch_gemm_ring_ta(Fmt ab, Fmt c, bool trans_b, const GemmParams &p, hipStream_t stream);
 
+// Persistent short-K kernel (gemm_short_k.hip): C[z] = A[z] . B[z]^T with
+// 16-bit inputs and output of the same type, K = 64 or 128, M and N
+// multiples of 256, no bias, scale 1; every row and C 16-byte aligned, so
+// each tile is whole and every epilogue store is a vector store.  `grid`
+// workgroups (a multiple of 8) walk the tiles.
+hipError_t launch_gemm_short_k(Fmt ab, const GemmParams &p, unsigned grid, hipStream_t stream);
+
 // C = act(bias + beta * old C) (bias, beta default none) for the K == 0
 // empty sum.
 hipError_t launch_fill(Fmt c, const GemmParams &p, hipStream_t stream);
