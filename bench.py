@@ -426,7 +426,8 @@ CSRC = os.path.join(ROOT, "tiled_matrix_multiplication_amd", "csrc")
 # Sources that define each workload's dominant kernel (the host dispatch and
 # the shared parameter header are not part of it).
 KERNEL_SOURCES = {
-    "gemm": ["gemm_mfma.h", "gemm_ring.h", "gemm_f32.hip", "gemm_bf16.hip", "gemm_f16.hip", "gemm_f8.hip"],
+    "gemm": ["gemm_mfma.h", "gemm_ring.h", "gemm_f32.hip", "gemm_bf16.hip", "gemm_f16.hip", "gemm_f8.hip",
+             "gemm_ring_ta.hip", "gemm_short_k.hip"],
     "gemv": ["gemv.hip"],
     "skinny": ["gemm_skinny.hip"],
     "attention": ["attention.hip"],
