@@ -22,6 +22,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "tmm_internal.h"
 
 namespace tmm {
@@ -167,11 +169,14 @@ void launch_vec(const GemvParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((gemv_vec_kernel<WT, YT, R, WPB, false>), dim3(blocks), dim3(64 * WPB), 0, stream, p);
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; callers may be
+// on several host threads).
 int gemv_cus() {
+  static std::mutex mu;
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
   if (cached[dev] == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
@@ -183,16 +188,16 @@ int gemv_cus() {
 
 // Rows per wave and waves per workgroup of the 16-byte path.  TMM_GEMV_CFG
 // = "R,W" (R in {1,2,4}, W in {4,8,16}) pins them for measurements.
+// Read once (a function-local static is initialised once, thread-safely).
 int gemv_cfg() {
-  static int cfg = -1;
-  if (cfg < 0) {
-    cfg = 0;
+  static const int cfg = [] {
     const char *s = getenv("TMM_GEMV_CFG");
     int r = 0, w = 0;
     if (s && sscanf(s, "%d,%d", &r, &w) == 2 && (r == 1 || r == 2 || r == 4) &&
         (w == 4 || w == 8 || w == 16))
-      cfg = r * 100 + w;
-  }
+      return r * 100 + w;
+    return 0;
+  }();
   return cfg;
 }
 
