@@ -435,13 +435,18 @@ KERNEL_SOURCES = {
 }
 
 
+# Largest M the library sends to its several-row GEMV (gemv.hip) rather than
+# the skinny MFMA kernel; the traffic hash and the counter filter follow it.
+GEMV_MULTI_MAX_M = 4
+
+
 def kernel_family(name):
     if name == "gemv":
         return "gemv"
     if name in ATTENTION:
         return "attention"
     if name.startswith("skinny"):
-        return "skinny"
+        return "gemv" if WORKLOADS[name][0] <= GEMV_MULTI_MAX_M else "skinny"
     if name in CONV:
         return "conv"
     return "gemm"
@@ -483,7 +488,7 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
                   kernel_substr="gemm_", copy_substr="copy"):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the workload's kernel by
     what the same counters read for a plain copy of `copy_bytes` bytes."""
-    if name == "gemv":
+    if kernel_family(name) == "gemv":
         kernel_substr = "gemv"
     elif name in ATTENTION:
         kernel_substr = "attn_fwd"

@@ -110,3 +110,44 @@ def test_every_skinny_tile(tmm, tile, monkeypatch):
     monkeypatch.setenv("TMM_SKINNY_TILE", tile)
     dC, o, T = gemm_case(tmm, 70, 300, 200, "bf16", "bf16", True, "normal", True, seed=900, pad=0)
     check(dC, o, T, 200, what=f"skinny tile {tile}")
+
+
+# (M, N, K, in, out, bias, pad): the several-row GEMV (2 <= M <= 8, K*E a
+# multiple of 16): whole 4096-element passes, a partial pass, several passes
+# with a partial one, ragged N, padded rows of X and W
+GEMVM = [
+    (2, 1000, 4096, "bf16", "bf16", True, 0),
+    (3, 4100, 1000, "f16", "f16", False, 8),
+    (4, 4096, 4096, "bf16", "f32", True, 0),
+    (5, 777, 8256, "f16", "f32", True, 0),
+    (8, 2048, 4104, "bf16", "bf16", True, 16),
+]
+
+
+@pytest.mark.parametrize("case", GEMVM, ids=[f"M{c[0]}-N{c[1]}-K{c[2]}-{c[3]}-{c[4]}" for c in GEMVM])
+@pytest.mark.parametrize("forced", [False, True], ids=["auto", "forced"])
+def test_gemv_multi(tmm, case, forced, monkeypatch):
+    """A few rows through one weight (Y = X . W^T): the several-row GEMV,
+    reached automatically and through TMM_FORCE_TILE=gemvm, against the
+    oracle."""
+    M, N, K, fmt, out, bias, pad = case
+    if forced:
+        monkeypatch.setenv("TMM_FORCE_TILE", "gemvm")
+    else:
+        monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+    dC, o, T = gemm_case(tmm, M, N, K, fmt, out, True, "normal", bias, seed=950 + 10 * GEMVM.index(case),
+                         pad=pad)
+    check(dC, o, T, K, what=f"gemv-multi M={M} N={N} K={K}")
+
+
+def test_gemv_multi_keeps_fp16_subnormals(tmm, monkeypatch):
+    """fp16 subnormal activations (2^-20) against unit weights: every output
+    is K * 2^-20 exactly, which a flush to zero would lose."""
+    monkeypatch.setenv("TMM_FORCE_TILE", "gemvm")
+    M, N, K = 4, 256, 4096
+    X = torch.full((M, K), 2.0 ** -20, dtype=torch.float16, device=DEV)
+    W = torch.ones((N, K), dtype=torch.float16, device=DEV)
+    Y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    tmm.tmm_gemm(X, W, Y, trans_b=True)
+    torch.cuda.synchronize()
+    assert torch.all(Y == K * 2.0 ** -20)

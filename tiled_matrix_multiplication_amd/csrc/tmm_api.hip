@@ -104,12 +104,13 @@ int cu_count() {
 }
 
 // TMM_FORCE_TILE = "256x256" | "256x128" | "128x128" | "256x256w4" | "256x256s2" |
-// "256x256r" | "skinny" | "generic" | "shortk" pins the tile shape for measurements and tile-by-tile
+// "256x256r" | "skinny" | "generic" | "shortk" | "gemvm" pins the tile shape for measurements and tile-by-tile
 // tests ("256x256s2": 256x256 tiles on the two-stage kernel only; "256x256r":
 // on the ring kernel wherever it applies, K-contiguous B included; "skinny":
 // the skinny-M kernel wherever it applies, any M; "generic": the any-layout
 // kernel for 16-bit inputs; "shortk": the persistent short-K kernel
-// wherever it applies, any tile count; with a transposed A, "256x256" and
+// wherever it applies, any tile count; "gemvm": the several-row GEMV
+// wherever it applies; with a transposed A, "256x256" and
 // "256x256r" pick the ring kernel wherever it applies).
 // Read on every call so that a test can switch it; anything else leaves the
 // choice to pick_tile.
@@ -130,6 +131,18 @@ bool forced_short_k() {
   const char *s = getenv("TMM_FORCE_TILE");
   return s && !strcmp(s, "shortk");
 }
+
+bool forced_gemv_multi() {
+  const char *s = getenv("TMM_FORCE_TILE");
+  return s && !strcmp(s, "gemvm");
+}
+
+// Largest M for which the several-row GEMV is chosen automatically: W 4096 x
+// 4096 fp16 + bias, graph-timed, against the skinny MFMA kernel: M = 2
+// 7.87 vs 8.81 us, M = 4 9.07 vs 9.17, M = 6 10.32 vs 9.44, M = 8 11.60 vs
+// 9.99 (its dot instructions and LDS reads of X grow with M and run after
+// the weight stream).  It takes up to 8 rows when forced.
+constexpr int64_t kGemvMultiMaxM = 4;
 
 // Largest M for which the skinny-M kernel is chosen automatically.
 constexpr int64_t kSkinnyMaxM = 256;
@@ -313,6 +326,15 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
       const bool va = aligned(A, 16) && (lda * e) % 16 == 0 && (batch == 1 || (sA * e) % 16 == 0);
       const bool vb = aligned(B, 16) && (ldb * e) % 16 == 0 && (batch == 1 || (sB * e) % 16 == 0);
       err = tmm::launch_gemm_generic((Fmt)ab, (Fmt)c, false, trans_b != 0, va, vb, p, stream);
+    } else if (vec && trans_b && plain && batch == 1 && (ab == TMM_BF16 || ab == TMM_F16) &&
+               M >= 2 && M <= 8 && (K * e) % 16 == 0 &&
+               (forced_gemv_multi() || (f < 0 && M <= kGemvMultiMaxM))) {
+      // Y = X . W^T for a few rows X: the weight stream of the GEMV with M
+      // dot products per weight chunk.
+      tmm::GemvMParams g;
+      g.N = N; g.K = K; g.W = B; g.ldw = ldb; g.x = A; g.ldx = lda; g.M = M;
+      g.y = C; g.ldy = ldc; g.bias = bias;
+      err = tmm::launch_gemv_multi((Fmt)ab, (Fmt)c, g, stream);
     } else if (short_k_ok(M, N, K, ab, c, trans_b, C, ldc, sC, batch, bias, plain, vec)) {
       const int64_t total = (M / 256) * (N / 256) * batch;
       const int64_t cus = cu_count();

@@ -98,6 +98,23 @@ struct GemvParams {
 
 hipError_t launch_gemv(Fmt w, Fmt y, bool vec, const GemvParams &p, hipStream_t stream);
 
+// Y[m] = W . X[m] (+ bias) for m < M, 2 <= M <= 8: X is M x K (row pitch
+// ldx), Y is M x N (row pitch ldy), W is N x K; 16-bit W and X, every row of
+// W and X 16-byte aligned and K*E a multiple of 16.
+struct GemvMParams {
+  int64_t N, K;
+  const void *W;
+  int64_t ldw;
+  const void *x;
+  int64_t ldx;
+  int64_t M;
+  void *y;
+  int64_t ldy;
+  const float *bias;
+};
+
+hipError_t launch_gemv_multi(Fmt w, Fmt y, const GemvMParams &p, hipStream_t stream);
+
 struct AttnParams {
   int64_t Z, Nq, Nk;
   const void *Q;
