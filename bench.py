@@ -364,6 +364,48 @@ def time_graph(run, launches, replays, warmup):
     return ms
 
 
+def gpu_state_under_load(run, seconds=1.0):
+    """GFX clock of each XCD and the socket power, read once by `amd-smi metric`
+    while `run` keeps the GPU busy back to back (after the timed region), or
+    None where amd-smi is missing or fails.  Under sustained load the clock
+    settles below its 2.4 GHz maximum, which the MFMA roofline's peak assumes."""
+    import subprocess
+    import threading
+
+    import torch
+    got = {}
+
+    def sample():
+        time.sleep(seconds / 2)
+        try:
+            r = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"],
+                               capture_output=True, text=True, timeout=15)
+            got["out"] = r.stdout
+        except Exception as e:  # noqa: BLE001 (any failure: report nothing)
+            got["err"] = repr(e)
+
+    th = threading.Thread(target=sample)
+    th.start()
+    t0 = time.perf_counter()
+    i = 0
+    while th.is_alive() and time.perf_counter() - t0 < seconds + 20:
+        for _ in range(8):
+            run(i)
+            i += 1
+        torch.cuda.synchronize()
+    th.join()
+    try:
+        d = json.loads(got["out"])
+        g = (d["gpu_data"] if isinstance(d, dict) else d)[0]
+        clocks = [v["clk"]["value"] for k, v in sorted(g["clock"].items())
+                  if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        power = g["power"]["socket_power"]["value"]
+        return {"gfx_clock_mhz": clocks, "socket_power_w": power,
+                "source": "amd-smi metric, read once while the timed kernel ran back to back"}
+    except Exception:  # noqa: BLE001
+        return None
+
+
 def copies_for(name):
     """Enough distinct input copies that a launch finds its operands out of the MALL."""
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
@@ -749,6 +791,8 @@ def main(argv=None):
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "weight_copies_rotated": g["copies"], "traffic": traffic_from_profile("gemv")}
         del g
+    if name == "square_bf16":
+        line["gpu_state"] = gpu_state_under_load(launcher(name, r["sets"], None, 1.0, 1.0))
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(name, r)
     line["wall_s_timed"] = round(r["wall"], 4)
