@@ -64,18 +64,41 @@ __device__ __forceinline__ uint16_t round16(float v) {
     return (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v, 0.f}, f16x2)) & 0xffffu);
 }
 
+// Elements [0, nv) of the 8 consecutive 16-bit elements at p (2-byte
+// aligned), zero past them, read as 4-byte words from the word boundary at
+// or below p: word j holds elements 2j - h and 2j - h + 1 (h = 1 when p is
+// two bytes past a boundary), it is read only when one of them is valid
+// (so no word past the last valid element's is touched), and each output
+// word is the 16-bit funnel shift of two neighbours.  5 word loads instead
+// of 8 two-byte loads, the same instructions for every alignment.
+__device__ __forceinline__ i32x4 load8_u16_words(const char *p, int nv) {
+  const int h = (int)(((uintptr_t)p >> 1) & 1);
+  const uint32_t *q = (const uint32_t *)(p - 2 * h);
+  uint32_t d[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int lo = 2 * j - h > 0 ? 2 * j - h : 0;
+    const bool ok = lo < nv && lo <= 2 * j - h + 1 && lo <= 7;
+    d[j] = ok ? q[j] : 0u;
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = (uint32_t)((((uint64_t)d[i + 1] << 32) | d[i]) >> (16 * h));
+    o[i] = 2 * i >= nv ? 0u : (2 * i + 1 < nv ? w : (w & 0xffffu));
+  }
+  return i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+}
+
 // 8 consecutive elements X[r][c .. c+7] of a row-major (rows x cols, ld)
-// matrix, zero outside it; one 16-byte load when whole and `vec`.
+// matrix, zero outside it; one 16-byte load when whole and `vec`, else
+// word loads of the valid part.
 __device__ __forceinline__ i32x4 load8(const uint16_t *X, int64_t ld, int64_t rows, int64_t cols,
                                        int64_t r, int64_t c, bool vec) {
   if (r < rows && c + 8 <= cols && vec) return *(const i32x4 *)(X + r * ld + c);
-  uint16_t e[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) e[j] = (r < rows && c + j < cols) ? X[r * ld + c + j] : (uint16_t)0;
-  i32x4 v;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = (int)((uint32_t)e[2 * j] | ((uint32_t)e[2 * j + 1] << 16));
-  return v;
+  const int64_t left = r < rows ? cols - c : 0;
+  const int nv = left <= 0 ? 0 : (left >= 8 ? 8 : (int)left);
+  return load8_u16_words((const char *)(X + r * ld + c), nv);
 }
 
 // One operand tile into LDS as 64 K-contiguous rows of kPitch elements.

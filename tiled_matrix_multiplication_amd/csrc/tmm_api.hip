@@ -322,11 +322,12 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
       return s && !strcmp(s, "generic");
     }();
     // Rows that are not 16-byte aligned (K or N not a multiple of 8 16-bit
-    // elements, e.g. 1000 x 3000 x 777) leave the tiled kernels on element
-    // loads; with an N-contiguous B the any-layout kernel's 64 x 64 tiles
-    // measured faster (bf16 NN, eager: 1000x3000x777 81 -> 54 us,
-    // 4097x511x1023 109 -> 105, 300x5000x1001 98 -> 55, 2000x2000x2001
-    // 265 -> 172); with a K-contiguous B they were not (78 -> 80, 108 -> 119).
+    // elements, e.g. 1000 x 3000 x 777) leave the tiled kernels on word
+    // loads over 128 x 128 tiles.  With an N-contiguous B the any-layout
+    // kernel's 64 x 64 tiles measured faster with operands cold in L2
+    // (bf16: 1000x3000x777 81.1 -> 57.4 us, 4097x511x1023 122.4 -> 102.8);
+    // with a K-contiguous B not clearly (eager, warm: 59 / 59, 77 / 102,
+    // 72 / 63, 234 / 225 us), so NT keeps the tiled kernel.
     const bool ragged_nn = !vec && !trans_b && f < 0 && (ab == TMM_BF16 || ab == TMM_F16);
     if ((generic_forced || ragged_nn) && (ab == TMM_BF16 || ab == TMM_F16)) {
       const int e = elem_bytes(ab);
