@@ -89,3 +89,14 @@ def test_integer_inputs_exact(tmm):
 
 def test_without_scale_and_bias(tmm):
     run(tmm, 2, 8, 8, 16, 32, 3, 3, 1, "bf16", "f32", False, 1, seed=2300, scale=False, bias=False)
+
+
+@pytest.mark.parametrize("case", [
+    (17, 31, 31, 8, 520, 3, 3, 1, "bf16", "bf16", True, 1),   # pixels end mid-tile, K not a multiple of 64
+    (16, 32, 32, 16, 512, 3, 3, 1, "f16", "f32", True, 2),    # pooled windows
+], ids=["17x31x31x8-520-ragged", "16x32x32x16-512-pool2"])
+def test_large_grids_take_wide_waves(tmm, case):
+    """Problems with at least two 256-pixel workgroups per CU run 64 pixels
+    per wave (the other tests' grids are smaller and run 32)."""
+    N, H, W, C, K, R, S, pad, fmt, out, relu, pool = case
+    run(tmm, N, H, W, C, K, R, S, pad, fmt, out, relu, pool, seed=2400)

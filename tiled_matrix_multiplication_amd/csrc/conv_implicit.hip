@@ -17,8 +17,9 @@
 //     window (4 consecutive rows = one 2 x 2 window), so the 4 accumulator
 //     rows a lane holds in a v_mfma_f32_16x16x32 block are exactly one
 //     pooling window of one filter and the max needs no data exchange;
-//   * a workgroup computes 128 pixels x 64 filters, 4 waves of 32 pixels x 64
-//     filters (2 x 4 blocks), over K-steps of 32 (r, s, c) elements; operand
+//   * a workgroup computes 128 or 256 pixels x 64 filters, 4 waves of 32 or
+//     64 pixels x 64 filters (2 or 4 x 4 blocks), over K-steps of 32 (r, s,
+//     c) elements; operand
 //     pieces are loaded into registers P steps ahead; each lane steps its own
 //     (r, s, c) position forward by 32 per step;
 //   * the weights are K-contiguous rows (the second operand directly);
@@ -39,10 +40,8 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128;  // pixels per workgroup
 constexpr int kBN = 64;   // filters per workgroup
 constexpr int kKS = 32;   // (r, s, c) elements per step
-constexpr int kFM = 2;    // 16-pixel blocks per wave
 constexpr int kFN = 4;    // 16-filter blocks per wave
 constexpr int kP = 3;     // steps of operands in flight
 
@@ -88,8 +87,11 @@ __device__ __forceinline__ void advance(Tap &t, int C, int S) {
   }
 }
 
-template <int AB, int CT>
+// FM: 16-pixel blocks per wave (2 or 4), so a workgroup covers 64 FM pixels.
+template <int AB, int CT, int FM>
 __global__ __launch_bounds__(256, 2) void conv_implicit_kernel(ConvParams p) {
+  constexpr int kFM = FM;
+  constexpr int kBM = 64 * FM;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kq = lane >> 4;
@@ -235,11 +237,27 @@ __global__ __launch_bounds__(256, 2) void conv_implicit_kernel(ConvParams p) {
   }
 }
 
+// 64 pixels per wave (FM = 4: each weight piece feeds 4 pixel blocks
+// instead of 2, a third fewer loads per matrix instruction) when that still
+// gives two workgroups per CU; 32 otherwise.  64 x 64^2 x 64 -> 128, 3x3,
+// pool: 204.8 -> 147.8 us; the 8 x 64^2 x 32 -> 64 problem (128 tiles of 256
+// pixels) measured 9.8 us with 32 and 12.8 us with 64.
 template <int AB, int CT>
 hipError_t launch_typed(const ConvParams &p, hipStream_t stream) {
   const int64_t P = p.H + 2 * p.pad - p.R + 1, Q = p.W + 2 * p.pad - p.S + 1;
-  const int64_t tiles = ((p.N * P * Q + kBM - 1) / kBM) * ((p.K + kBN - 1) / kBN);
-  hipLaunchKernelGGL((conv_implicit_kernel<AB, CT>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  const int64_t tn = (p.K + kBN - 1) / kBN;
+  const int64_t t256 = ((p.N * P * Q + 255) / 256) * tn;
+  int cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (t256 >= 2 * (int64_t)cus) {
+    hipLaunchKernelGGL((conv_implicit_kernel<AB, CT, 4>), dim3((unsigned)t256), dim3(256), 0, stream, p);
+  } else {
+    const int64_t t128 = ((p.N * P * Q + 127) / 128) * tn;
+    hipLaunchKernelGGL((conv_implicit_kernel<AB, CT, 2>), dim3((unsigned)t128), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
