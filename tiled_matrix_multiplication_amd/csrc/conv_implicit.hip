@@ -247,12 +247,7 @@ hipError_t launch_typed(const ConvParams &p, hipStream_t stream) {
   const int64_t P = p.H + 2 * p.pad - p.R + 1, Q = p.W + 2 * p.pad - p.S + 1;
   const int64_t tn = (p.K + kBN - 1) / kBN;
   const int64_t t256 = ((p.N * P * Q + 255) / 256) * tn;
-  int cus = 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  if (t256 >= 2 * (int64_t)cus) {
+  if (t256 >= 2 * (int64_t)device_cu_count()) {
     hipLaunchKernelGGL((conv_implicit_kernel<AB, CT, 4>), dim3((unsigned)t256), dim3(256), 0, stream, p);
   } else {
     const int64_t t128 = ((p.N * P * Q + 127) / 128) * tn;

@@ -22,8 +22,6 @@
 #include <stdio.h>
 #include <stdlib.h>
 
-#include <mutex>
-
 #include "tmm_internal.h"
 
 namespace tmm {
@@ -272,23 +270,6 @@ void launch_vec(const GemvParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((gemv_vec_kernel<WT, YT, R, WPB, false>), dim3(blocks), dim3(64 * WPB), 0, stream, p);
 }
 
-// Compute units of the current device (cached per device; callers may be
-// on several host threads).
-int gemv_cus() {
-  static std::mutex mu;
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 // Rows per wave and waves per workgroup of the 16-byte path.  TMM_GEMV_CFG
 // = "R,W" (R in {1,2,4}, W in {4,8,16}) pins them for measurements.
 // Read once (a function-local static is initialised once, thread-safely).
@@ -321,7 +302,7 @@ hipError_t launch_typed(bool vec, const GemvParams &p, hipStream_t stream) {
         // One row per wave; sixteen waves per workgroup once that still
         // gives every CU a workgroup (W 4096 x 4096 bf16: 6.87 against
         // 7.01 us per launch for four), four below (more CUs streaming).
-        if (p.N >= 16 * (int64_t)gemv_cus()) launch_vec<WT, YT, 1, 16>(p, stream);
+        if (p.N >= 16 * (int64_t)device_cu_count()) launch_vec<WT, YT, 1, 16>(p, stream);
         else launch_vec<WT, YT, 1, 4>(p, stream);
         break;
     }

@@ -15,6 +15,28 @@
 #include "tmm.h"
 #include "tmm_internal.h"
 
+namespace tmm {
+
+// Compute units of the current device (cached per device; callers may be on
+// several host threads).
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace tmm
+
 namespace {
 
 using tmm::Fmt;
@@ -86,22 +108,7 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, cons
   return TMM_OK;
 }
 
-// Compute units of the current device (cached per device).
-int cu_count() {
-  static std::mutex mu;
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
+int cu_count() { return tmm::device_cu_count(); }
 
 // TMM_FORCE_TILE = "256x256" | "256x128" | "128x128" | "256x256w4" | "256x256s2" |
 // "256x256r" | "skinny" | "generic" | "shortk" | "gemvm" pins the tile shape for measurements and tile-by-tile

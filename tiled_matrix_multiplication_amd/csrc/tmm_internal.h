@@ -7,6 +7,9 @@
 
 namespace tmm {
 
+// Compute units of the current device (cached per device, thread-safe).
+int device_cu_count();
+
 // Element formats, same numbering as tmm_dtype in include/tmm.h.
 enum Fmt : int { kF32 = 0, kBF16 = 1, kF16 = 2, kF8 = 3 };
 
