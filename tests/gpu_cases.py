@@ -6,6 +6,7 @@ import torch
 
 import oracle
 import synthetic as syn
+from parity import f8_operands
 
 DEV = "cuda:0"
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
@@ -34,7 +35,8 @@ def make_operand(shape, fmt, dist, seed, pad=0, scale=None):
     return bits, bits[:, :cols], s
 
 
-def gemm_case(tmm, M, N, K, fmt, out, trans_b, dist, bias, seed=0, pad=0):
+def gemm_case(tmm, M, N, K, fmt, out, trans_b, dist, bias, seed=0, pad=0, want_ops=False):
+    """(C on the GPU, oracle o, oracle T[, fp8 operands for parity.check or None])."""
     A_full, A, sa = make_operand((M, K), fmt, dist, seed + 1, pad)
     bshape = (N, K) if trans_b else (K, N)
     B_full, B, sb = make_operand(bshape, fmt, dist, seed + 2, pad)
@@ -49,4 +51,7 @@ def gemm_case(tmm, M, N, K, fmt, out, trans_b, dist, bias, seed=0, pad=0):
     dbias = torch.from_numpy(bvec).to(DEV) if bvec is not None else None
     tmm.tmm_gemm(dA, dB, dC, bias=dbias, trans_b=trans_b, scale_a=float(sa), scale_b=float(sb))
     torch.cuda.synchronize()
+    if want_ops:
+        ops = f8_operands(A, B, trans_b, float(sa) * float(sb)) if fmt == "e4m3" else None
+        return dC, o, T, ops
     return dC, o, T

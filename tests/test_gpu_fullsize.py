@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synthetic as syn
-from parity import check
+from parity import check, f8_operands
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -35,11 +35,17 @@ def sampled_check(C, A, B, fmt, trans_b, bias=None, sa=1.0, sb=1.0, nrows=32, nc
     J = np.sort(g.choice(N, size=min(ncols, N), replace=False))
     o_r, t_r = oracle.gemm(fmt, np.ascontiguousarray(A[I]), B, trans_b=trans_b, bias=bias,
                            scale_a=sa, scale_b=sb, want_abs=True)
-    check(C[torch.as_tensor(I, device=C.device)], o_r, t_r, K, what=f"{what} rows", f8=f8)
+    ops_r = ops_c = None
+    if f8:
+        qa, qb, sc = f8_operands(A, B, trans_b, sa * sb)
+        ops_r = (qa[I], qb, sc)
+        ops_c = (qa, qb[:, J], sc)
+    check(C[torch.as_tensor(I, device=C.device)], o_r, t_r, K, what=f"{what} rows", f8=f8, f8_ops=ops_r)
     Bj = np.ascontiguousarray(B[J]) if trans_b else np.ascontiguousarray(B[:, J])
     bj = None if bias is None else np.ascontiguousarray(bias[J])
     o_c, t_c = oracle.gemm(fmt, A, Bj, trans_b=trans_b, bias=bj, scale_a=sa, scale_b=sb, want_abs=True)
-    check(C[:, torch.as_tensor(J, device=C.device)].contiguous(), o_c, t_c, K, what=f"{what} cols", f8=f8)
+    check(C[:, torch.as_tensor(J, device=C.device)].contiguous(), o_c, t_c, K, what=f"{what} cols", f8=f8,
+          f8_ops=ops_c)
 
 
 def test_square_bf16_4096(tmm):

@@ -12,7 +12,7 @@ import torch
 import oracle
 import synthetic as syn
 from gpu_cases import DEV, TORCH_DT, on_gpu
-from parity import check, to_bits
+from parity import check, f8_operands, to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +58,11 @@ def run_case(tmm, M, N, K, fmt, out, ta, tb, alpha, beta, relu, bias, seed, dist
         cin = oracle.decode(out, C0[z])
         o, T = oracle.gemm_ex(fmt, As[z], Bs[z], ta, tb, a_eff, beta, cin if beta else None, bvec, relu,
                               want_abs=True)
-        check(dC[z], o, T, K, exact=(dist == "int"), what=f"{what} z {z}", f8=(fmt == "e4m3"))
+        ops = None
+        if fmt == "e4m3":
+            qa, qb, _ = f8_operands(As[z], Bs[z], tb, 1.0)
+            ops = (qa.T if ta else qa, qb, a_eff)
+        check(dC[z], o, T, K, exact=(dist == "int"), what=f"{what} z {z}", f8=(fmt == "e4m3"), f8_ops=ops)
 
 
 LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]

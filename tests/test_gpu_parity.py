@@ -61,8 +61,9 @@ def _id(c):
 @pytest.mark.parametrize("case", CASES, ids=[_id(c) for c in CASES])
 def test_gemm_parity(tmm, case):
     M, N, K, fmt, out, tb, dist, bias, pad = case
-    dC, o, T = gemm_case(tmm, M, N, K, fmt, out, tb, dist, bias, seed=10 * CASES.index(case), pad=pad)
-    check(dC, o, T, K, exact=(dist == "int"), what=_id(case), f8=(fmt == "e4m3"))
+    dC, o, T, ops = gemm_case(tmm, M, N, K, fmt, out, tb, dist, bias, seed=10 * CASES.index(case), pad=pad,
+                              want_ops=True)
+    check(dC, o, T, K, exact=(dist == "int"), what=_id(case), f8=(fmt == "e4m3"), f8_ops=ops)
 
 
 RAGGED = [(1000, 3000, 777), (4097, 511, 1023)]

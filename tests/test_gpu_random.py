@@ -9,7 +9,7 @@ import torch
 import oracle
 import synthetic as syn
 from gpu_cases import DEV, TORCH_DT, on_gpu
-from parity import check
+from parity import check, f8_operands
 
 pytestmark = pytest.mark.gpu
 
@@ -75,7 +75,8 @@ def test_random_problem(tmm, i, monkeypatch):
         A = np.ascontiguousarray(Ab[z][:, :K])
         B = np.ascontiguousarray(Bb[z][:, :(K if tb else N)])
         o, T = oracle.gemm(fmt, A, B, trans_b=tb, bias=bvec, scale_a=sa, scale_b=sb, want_abs=True)
-        check(C[z], o, T, K, what=f"{what} z {z}", f8=(fmt == "e4m3"))
+        ops = f8_operands(A, B, tb, float(sa) * float(sb)) if fmt == "e4m3" else None
+        check(C[z], o, T, K, what=f"{what} z {z}", f8=(fmt == "e4m3"), f8_ops=ops)
 
 
 @pytest.fixture(scope="module")

@@ -55,9 +55,10 @@ def test_every_tile(tmm, case, monkeypatch):
     first = None
     for tile in TILES:
         monkeypatch.setenv("TMM_FORCE_TILE", tile)
-        dC, o, T = gemm_case(tmm, M, N, K, fmt, out, tb, dist, bias,
-                             seed=100 + 10 * CASES.index(case), pad=pad)
-        check(dC, o, T, K, exact=(dist == "int"), what=f"{_id(case)} tile {tile}", f8=(fmt == "e4m3"))
+        dC, o, T, ops = gemm_case(tmm, M, N, K, fmt, out, tb, dist, bias,
+                                  seed=100 + 10 * CASES.index(case), pad=pad, want_ops=True)
+        check(dC, o, T, K, exact=(dist == "int"), what=f"{_id(case)} tile {tile}", f8=(fmt == "e4m3"),
+              f8_ops=ops)
         bits = dC.view(torch.int32 if dC.element_size() == 4 else torch.int16)
         if first is None:
             first = bits

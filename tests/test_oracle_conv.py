@@ -102,3 +102,51 @@ def test_pooled_is_max_of_unpooled_and_abs_companion():
 def test_rejects_odd_pooling():
     with pytest.raises(ValueError):
         oracle.conv2d("f16", f16(np.ones((1, 5, 5, 2))), f16(np.ones((1, 3, 3, 2))), 1, pool=2)
+
+
+@pytest.mark.parametrize("pool", [1, 2])
+def test_abs_companion_equals_output_for_nonnegative_terms(pool):
+    """With x, w, scale and bias all >= 0 every term is >= 0, so the
+    companion |scale| sum |w x| + |bias| is the output itself, exactly --
+    unpooled and as the largest over each 2 x 2 window."""
+    g = np.random.default_rng(21 + pool)
+    xb = f16(np.abs(g.normal(size=(2, 6, 8, 5))))
+    wb = f16(np.abs(g.normal(size=(4, 3, 3, 5))))
+    scale = np.abs(g.normal(size=4)).astype(np.float32)
+    bias = np.abs(g.normal(size=4)).astype(np.float32)
+    o, T = oracle.conv2d("f16", xb, wb, 1, scale, bias, False, pool, want_abs=True)
+    assert np.array_equal(T, o)
+    assert np.all(o > 0)
+
+
+def test_abs_companion_sign_terms_exact():
+    """Small integers (exact in float64): x >= 0, w <= 0 and a negative
+    scale give |scale| sum |w x| = scale * sum w x; a negative bias adds
+    2 |bias| to the companion: T = o + 2 |bias| (no ReLU, no pooling)."""
+    g = np.random.default_rng(31)
+    x = g.integers(0, 5, size=(1, 5, 6, 3)).astype(np.float64)
+    w = -g.integers(0, 5, size=(2, 3, 3, 3)).astype(np.float64)
+    scale = np.array([-2.0, -0.5], dtype=np.float32)
+    bias = np.array([-3.0, -1.0], dtype=np.float32)
+    o, T = oracle.conv2d("f16", f16(x), f16(w), 1, scale, bias, False, 1, want_abs=True)
+    assert np.array_equal(T, o + 2 * np.abs(bias.astype(np.float64))[None, None, None, :])
+    # and the numpy brute force gives the same o (so T is pinned, not o against itself)
+    assert np.array_equal(o, numpy_conv(x, w, 1, scale.astype(np.float64), bias.astype(np.float64),
+                                        False, 1))
+
+
+def test_pooled_companion_is_window_max_of_companions():
+    """Mixed signs: the pooled companion is the largest unpooled companion of
+    its 2 x 2 window, and the unpooled one is |scale| (|w| conv |x|) + |bias|
+    from the numpy brute force on absolute values (small integers: exact)."""
+    g = np.random.default_rng(41)
+    x = g.integers(-4, 5, size=(2, 6, 4, 3)).astype(np.float64)
+    w = g.integers(-4, 5, size=(3, 3, 3, 3)).astype(np.float64)
+    scale = np.array([1.5, -2.0, 0.25], dtype=np.float32)
+    bias = np.array([-1.0, 2.0, 0.0], dtype=np.float32)
+    _, T1 = oracle.conv2d("f16", f16(x), f16(w), 1, scale, bias, True, 1, want_abs=True)
+    _, T2 = oracle.conv2d("f16", f16(x), f16(w), 1, scale, bias, True, 2, want_abs=True)
+    ref = numpy_conv(np.abs(x), np.abs(w), 1, np.abs(scale.astype(np.float64)),
+                     np.abs(bias.astype(np.float64)), False, 1)
+    assert np.array_equal(T1, ref)
+    assert np.array_equal(T2, ref.reshape(2, 3, 2, 2, 2, 3).max(axis=(2, 4)))

@@ -100,3 +100,33 @@ def test_rejects_bad_arguments():
         oracle.gemm_ex("f16", A, f16(np.ones((4, 5))))
     with pytest.raises(ValueError):
         oracle.gemm_ex("f16", A, f16(np.ones((3, 2))), C_in=np.zeros((3, 3)), beta=1.0)
+
+
+@pytest.mark.parametrize("ta,tb", list(itertools.product([False, True], repeat=2)))
+def test_abs_companion_exact_with_bias_and_beta(ta, tb):
+    """T = |alpha| |a'| |b'| + |bias| + |beta c| exactly on small integers
+    (numpy's float64 product of the absolute values is exact here), with a
+    negative alpha, beta and mixed-sign bias and C."""
+    M, N, K = 5, 7, 9
+    g = np.random.default_rng([51, ta, tb])
+    a = g.integers(-4, 5, size=(M, K)).astype(np.float64)
+    b = g.integers(-4, 5, size=(K, N)).astype(np.float64)
+    A = f16(a.T if ta else a)
+    B = f16(b.T if tb else b)
+    bias = g.integers(-4, 5, size=N).astype(np.float32)
+    Cin = g.integers(-4, 5, size=(M, N)).astype(np.float64)
+    o, T = oracle.gemm_ex("f16", A, B, trans_a=ta, trans_b=tb, alpha=-1.5, beta=-0.75, C_in=Cin,
+                          bias=bias, want_abs=True)
+    want_T = 1.5 * (np.abs(a) @ np.abs(b)) + np.abs(bias.astype(np.float64))[None, :] + 0.75 * np.abs(Cin)
+    assert np.array_equal(T, want_T)
+    assert np.array_equal(o, -1.5 * (a @ b) + bias.astype(np.float64)[None, :] - 0.75 * Cin)
+
+
+def test_abs_companion_equals_output_for_nonnegative_terms():
+    """alpha, a, b, bias, beta and C all >= 0: every term is >= 0, so T = o exactly."""
+    g = np.random.default_rng(52)
+    A, B = f16(np.abs(g.normal(size=(6, 11)))), f16(np.abs(g.normal(size=(11, 4))))
+    bias = np.abs(g.normal(size=4)).astype(np.float32)
+    Cin = np.abs(g.normal(size=(6, 4)))
+    o, T = oracle.gemm_ex("f16", A, B, alpha=0.75, beta=1.25, C_in=Cin, bias=bias, want_abs=True)
+    assert np.array_equal(T, o)
