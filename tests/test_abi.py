@@ -35,12 +35,25 @@ def test_library_exports_every_declared_symbol(tmm):
     assert set(tmm.EXPORTS) == set(declared_functions())
 
 
+def declared_status_codes():
+    """{value: name} of the status enum in include/tmm.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return {int(v): n for n, v in re.findall(r"\b(TMM_(?:OK|ERR_[A-Z]+))\s*=\s*(-?\d+)", text)}
+
+
 def test_version_and_status_strings(tmm):
     assert tmm.tmm_version() == 10000
-    for code in range(-8, 1):
+    codes = declared_status_codes()
+    assert sorted(codes) == list(range(-9, 1))
+    for code in codes:
         s = tmm.tmm_status_string(code)
         assert s and s != "unknown status code", code
     assert tmm.tmm_status_string(-99) == "unknown status code"
+
+
+def test_binding_names_every_status_code(tmm):
+    """The binding's STATUS map is the header's enum, name for name."""
+    assert tmm.STATUS == declared_status_codes()
 
 
 FAKE = ctypes.c_void_p(0x100000)     # never dereferenced: every call below fails validation

@@ -1,0 +1,25 @@
+"""The misaligned 16-bit piece loader of the kernels (load8_u16_words in
+tiled_matrix_multiplication_amd/csrc/load_words.h, compiled for the host
+from the same header) reads nothing past the word holding the last valid
+element, for both alignments and every valid count, and returns the right
+values: tests/load_words_check.hip puts that word against a guard page."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_load8_u16_words_stays_before_the_guard_page(tmp_path):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path / "load_words_check")
+    subprocess.run([hipcc, "-x", "hip", "--offload-host-only", "-O2", "-std=c++17",
+                    "-I", os.path.join(ROOT, "tiled_matrix_multiplication_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "load_words_check.hip"), "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, f"rc {r.returncode}: {r.stdout} {r.stderr}"
+    assert r.stdout.startswith("OK 20 windows"), r.stdout

@@ -22,6 +22,7 @@ TMM_F32, TMM_BF16, TMM_F16, TMM_F8E4M3 = 0, 1, 2, 3
 STATUS = {
     0: "TMM_OK", -1: "TMM_ERR_DIM", -2: "TMM_ERR_LD", -3: "TMM_ERR_NULL", -4: "TMM_ERR_DTYPE",
     -5: "TMM_ERR_SCALE", -6: "TMM_ERR_STRIDE", -7: "TMM_ERR_ALIGN", -8: "TMM_ERR_LAUNCH",
+    -9: "TMM_ERR_ARG",
 }
 
 EXPORTS = ("tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemm_ex", "tmm_gemv", "tmm_attention_fwd",

@@ -17,6 +17,7 @@
 // K are read as zero; outputs past M or N are not stored.
 #include <stdint.h>
 
+#include "load_words.h"
 #include "tmm_internal.h"
 
 namespace tmm {
@@ -64,31 +65,7 @@ __device__ __forceinline__ uint16_t round16(float v) {
     return (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v, 0.f}, f16x2)) & 0xffffu);
 }
 
-// Elements [0, nv) of the 8 consecutive 16-bit elements at p (2-byte
-// aligned), zero past them, read as 4-byte words from the word boundary at
-// or below p: word j holds elements 2j - h and 2j - h + 1 (h = 1 when p is
-// two bytes past a boundary), it is read only when one of them is valid
-// (so no word past the last valid element's is touched), and each output
-// word is the 16-bit funnel shift of two neighbours.  5 word loads instead
-// of 8 two-byte loads, the same instructions for every alignment.
-__device__ __forceinline__ i32x4 load8_u16_words(const char *p, int nv) {
-  const int h = (int)(((uintptr_t)p >> 1) & 1);
-  const uint32_t *q = (const uint32_t *)(p - 2 * h);
-  uint32_t d[5];
-#pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    const int lo = 2 * j - h > 0 ? 2 * j - h : 0;
-    const bool ok = lo < nv && lo <= 2 * j - h + 1 && lo <= 7;
-    d[j] = ok ? q[j] : 0u;
-  }
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = (uint32_t)((((uint64_t)d[i + 1] << 32) | d[i]) >> (16 * h));
-    o[i] = 2 * i >= nv ? 0u : (2 * i + 1 < nv ? w : (w & 0xffffu));
-  }
-  return i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-}
+// load8_u16_words: the misaligned 16-bit piece loader of load_words.h.
 
 // 8 consecutive elements X[r][c .. c+7] of a row-major (rows x cols, ld)
 // matrix, zero outside it; one 16-byte load when whole and `vec`, else
