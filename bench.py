@@ -364,24 +364,48 @@ def time_graph(run, launches, replays, warmup):
     return ms
 
 
+def _smi_handle(amdsmi):
+    """The amdsmi handle of cuda:0 (matched by PCI address where torch
+    reports it, else the first GPU amdsmi lists)."""
+    import torch
+    handles = amdsmi.amdsmi_get_processor_handles()
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        want = (int(pr.pci_domain_id), int(pr.pci_bus_id), int(pr.pci_device_id))
+        for h in handles:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "dddd:bb:dd.f"
+            dom, bus, rest = bdf.split(":")
+            if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                return h
+    except Exception:  # noqa: BLE001 (older torch without PCI fields)
+        pass
+    return handles[0]
+
+
 def gpu_state_under_load(run, seconds=1.0):
-    """GFX clock of each XCD and the socket power, read once by `amd-smi metric`
-    while `run` keeps the GPU busy back to back (after the timed region), or
-    None where amd-smi is missing or fails.  Under sustained load the clock
-    settles below its 2.4 GHz maximum, which the MFMA roofline's peak assumes."""
-    import subprocess
+    """GFX clock of each XCD and the socket power while `run` keeps the GPU
+    busy back to back (after the timed region), read in this process through
+    the amdsmi library (no other program is started), or None where it is
+    missing or fails.  Under sustained load the clock may settle below its
+    2.4 GHz maximum, which the MFMA roofline's peak assumes."""
     import threading
 
     import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = _smi_handle(amdsmi)
+    except Exception:  # noqa: BLE001 (any failure: report nothing)
+        return None
     got = {}
 
     def sample():
         time.sleep(seconds / 2)
         try:
-            r = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"],
-                               capture_output=True, text=True, timeout=15)
-            got["out"] = r.stdout
-        except Exception as e:  # noqa: BLE001 (any failure: report nothing)
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            got["clocks"] = [int(c) for c in m["current_gfxclks"] if isinstance(c, int) and 0 < c < 65535]
+            got["power"] = m.get("current_socket_power")
+        except Exception as e:  # noqa: BLE001
             got["err"] = repr(e)
 
     th = threading.Thread(target=sample)
@@ -395,15 +419,15 @@ def gpu_state_under_load(run, seconds=1.0):
         torch.cuda.synchronize()
     th.join()
     try:
-        d = json.loads(got["out"])
-        g = (d["gpu_data"] if isinstance(d, dict) else d)[0]
-        clocks = [v["clk"]["value"] for k, v in sorted(g["clock"].items())
-                  if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
-        power = g["power"]["socket_power"]["value"]
-        return {"gfx_clock_mhz": clocks, "socket_power_w": power,
-                "source": "amd-smi metric, read once while the timed kernel ran back to back"}
+        amdsmi.amdsmi_shut_down()
     except Exception:  # noqa: BLE001
+        pass
+    if not got.get("clocks"):
         return None
+    power = got.get("power")
+    return {"gfx_clock_mhz": got["clocks"],
+            "socket_power_w": power if isinstance(power, int) and 0 < power < 65535 else None,
+            "source": "amdsmi GPU metrics (in process), read once while the timed kernel ran back to back"}
 
 
 def copies_for(name):
@@ -620,12 +644,57 @@ def cpu_baseline(name, r, target_s=20.0):
     C = r["sets"][0][2]
     C0 = C[0] if Z > 1 else C
     err = compare_rows(C0, idx, o)
-    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+    line = {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
             "kind": "oracle", "seconds": round(t, 2),
             "sample": (f"{len(idx)} of {M} rows" if len(idx) < M else f"all {M} rows") +
                       f" of the {describe(name)} product ({len(idx)}x{N}x{K}, fp64 triple loop; "
                       f"time includes decoding the inputs)",
-            "sample_rel_fro_vs_gpu": err}
+            "sample_rel_fro_vs_gpu": err, **host_cpus()}
+    if name == "square_bf16":
+        line["single_core"] = single_core_1024()
+        line["page_context"] = page_cpu_figures()
+    return line
+
+
+def host_cpus():
+    """CPUs of the host: all of them, and those this process may run on."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except Exception:  # noqa: BLE001
+        usable = os.cpu_count()
+    return {"nproc": usable, "host_cpus": os.cpu_count()}
+
+
+def single_core_1024():
+    """The oracle on one thread for a 1024^3 bf16 product (the same inputs'
+    recipe as the square workload), and that time times 64 -- the 4096^3
+    product has 64 times the multiply-adds -- as the one-core estimate."""
+    import oracle
+    import synthetic as syn
+    n = 1024
+    A = syn.to_bits(syn.normal((n, n), syn.seed_of(2, "A")), "bf16")
+    B = syn.to_bits(syn.normal((n, n), syn.seed_of(2, "B")), "bf16")
+    before = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.gemm("bf16", A, B)
+        t = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(before)
+    return {"seconds_1024": round(t, 3), "tflops": round(gemm_flops(n, n, n) / t / 1e12, 6), "threads": 1,
+            "extrapolated_4096_seconds": round(64 * t, 1),
+            "note": "4096^3 has 64x the multiply-adds of 1024^3"}
+
+
+def page_cpu_figures():
+    """The pages' CPU FP32 times for N = 4096 (context only)."""
+    try:
+        with open(os.path.join(ROOT, "tests", "golden", "page_figures.json")) as f:
+            d = json.load(f)["cpu_fp32_4096_seconds"]
+        return {"seconds": d["printed"], "source": d["source"].split(":")[0]}
+    except Exception:  # noqa: BLE001
+        return None
 
 
 def cpu_baseline_full(name, r, target_s=20.0):

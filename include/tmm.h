@@ -227,6 +227,29 @@ const char *tmm_status_string(int status);
 /* Library version as major*10000 + minor*100 + patch. */
 int tmm_version(void);
 
+/*
+ * Kernel-choice override, for measurements and kernel-by-kernel tests only;
+ * results are the same (within the stated tolerances) whatever it pins.
+ * `spec` is a list of key=value items separated by ';' or spaces, NULL or ""
+ * for none:
+ *   tile=256x256 | 256x128 | 128x128 | 256x256w4 | 256x256s2 | 256x256r |
+ *        skinny | generic | shortk | gemvm
+ *                  the GEMM kernel / tile shape wherever it applies
+ *                  (256x256s2: two-stage kernel only; 256x256r: the ring
+ *                  kernel, K-contiguous B included; skinny, generic, shortk,
+ *                  gemvm: the skinny-M, any-layout, short-K and several-row
+ *                  GEMV kernels)
+ *   skinny=<bm>x<bn>   skinny-M tile, bm and bn in {16, 32, 64}
+ *   gemv=<r>x<w>       GEMV rows per wave (1, 2, 4) and waves per workgroup
+ *                      (4, 8, 16)
+ * The same text in the environment variable TMM_OVERRIDE is read once, at
+ * the library's first call (an unparsable value pins nothing).  This call
+ * replaces the whole setting for every later call from any thread; calls
+ * already enqueued keep their kernels.  Returns TMM_OK, or TMM_ERR_ARG for
+ * an unknown key or value (the setting is then left as it was).
+ */
+int tmm_set_override(const char *spec);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,9 +65,10 @@ def _load():
     lib.oracle_conv2d.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp,
                                   ctypes.c_int, ctypes.c_int, vp, vp]
     lib.oracle_threads.argtypes = []
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_attention.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, vp, i64, vp, i64,
                                      ctypes.c_double, vp, i64, vp]
-    for f in (lib.oracle_decode, lib.oracle_round, lib.oracle_gemm, lib.oracle_threads,
+    for f in (lib.oracle_decode, lib.oracle_round, lib.oracle_gemm, lib.oracle_threads, lib.oracle_set_threads,
               lib.oracle_attention, lib.oracle_gemm_ex, lib.oracle_conv2d):
         f.restype = ctypes.c_int
     _lib = lib
@@ -249,6 +250,11 @@ def attention(fmt, Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
 def threads() -> int:
     """Threads the oracle's product runs on (OpenMP, from OMP_NUM_THREADS)."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> int:
+    """Run the oracle's loops on n threads from now on; returns the count in force."""
+    return int(_load().oracle_set_threads(int(n)))
 
 
 def _rowmajor(X: np.ndarray) -> np.ndarray:

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemm_ex", "tmm_gemv", "tmm_attention_fwd",
-         "tmm_conv2d_fused", "tmm_status_string", "tmm_version"])
+         "tmm_conv2d_fused", "tmm_status_string", "tmm_version", "tmm_set_override"])
 
 
 def test_library_exports_every_declared_symbol(tmm):
@@ -231,3 +231,17 @@ def test_conv_validation(tmm):
 
 def test_conv_quick_return(tmm):
     assert conv(tmm, N=0, x=None, w=None, out=None) == 0
+
+
+def test_override_accepts_the_documented_keys_and_rejects_others(tmm):
+    """tmm_set_override parses on the host (no HIP call); a bad item leaves
+    the setting as it was and returns TMM_ERR_ARG."""
+    try:
+        for spec in ["", "tile=128x128", "tile=skinny;skinny=32x64", "tile=gemvm", "gemv=2x16",
+                     "tile=shortk skinny=16x16 gemv=1x4", "tile=generic", "tile=256x256r"]:
+            assert tmm.lib.tmm_set_override(spec.encode()) == 0, spec
+        for spec in ["tile=99x99", "skinny=8x16", "gemv=3x4", "gemv=2,16", "foo=1", "tile", "tile=128x128;x"]:
+            assert tmm.lib.tmm_set_override(spec.encode()) == -9, spec
+        assert tmm.lib.tmm_set_override(None) == 0
+    finally:
+        tmm.tmm_set_override(None)

@@ -71,8 +71,8 @@ LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
 @pytest.mark.parametrize("ta,tb", LAYOUTS, ids=["NN", "NT", "TN", "TT"])
 @pytest.mark.parametrize("fmt,out", [("bf16", "bf16"), ("f16", "f32")])
 @pytest.mark.parametrize("M", [200, 300])
-def test_layouts(tmm, ta, tb, fmt, out, M, monkeypatch):
-    monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+def test_layouts(tmm, ta, tb, fmt, out, M, force):
+    force()
     relu = (M == 300)
     run_case(tmm, M, 150, 104, fmt, out, ta, tb, 0.5, -1.25, relu, True, seed=1000 + M,
              what=f"{'T' if ta else 'N'}{'T' if tb else 'N'} {fmt}->{out} M {M}")
@@ -83,19 +83,19 @@ TILES = ["256x256", "256x256r", "256x256s2", "256x256w4", "256x128", "128x128", 
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("tb", [False, True], ids=["NN", "NT"])
-def test_every_kernel(tmm, tile, tb, monkeypatch):
+def test_every_kernel(tmm, tile, tb, force):
     """The full-form epilogue of each kernel (the skinny kernel takes NT only;
     for NN the forced name falls back to the automatic choice)."""
-    monkeypatch.setenv("TMM_FORCE_TILE", tile)
+    force(tile)
     run_case(tmm, 520, 776, 320, "bf16", "bf16", False, tb, 1.5, 0.75, True, True, seed=1100,
              what=f"tile {tile} {'NT' if tb else 'NN'}")
 
 
-def test_integer_inputs_exact(tmm, monkeypatch):
+def test_integer_inputs_exact(tmm, force):
     """Small-integer inputs, alpha = 2, beta = -1, ReLU: every intermediate is
     an exact integer in fp32, so the output equals R(o) bit for bit -- in all
     four layouts."""
-    monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+    force()
     for ta, tb in LAYOUTS:
         run_case(tmm, 130, 270, 96, "bf16", "f32", ta, tb, 2.0, -1.0, True, True, seed=1200,
                  dist="int", what=f"int {ta}{tb}")
@@ -103,8 +103,8 @@ def test_integer_inputs_exact(tmm, monkeypatch):
                  dist="int", what=f"int f16 {ta}{tb}")
 
 
-def test_fp8_and_fp32(tmm, monkeypatch):
-    monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+def test_fp8_and_fp32(tmm, force):
+    force()
     run_case(tmm, 512, 512, 512, "e4m3", "bf16", False, False, 0.5, 1.0, True, True, seed=1300,
              what="fp8 NN")
     run_case(tmm, 384, 640, 200, "e4m3", "f32", False, True, 1.0, -0.5, False, True, seed=1310,
@@ -112,20 +112,20 @@ def test_fp8_and_fp32(tmm, monkeypatch):
     run_case(tmm, 130, 70, 50, "f32", "f32", False, True, -1.0, 2.0, True, True, seed=1320, what="fp32")
 
 
-def test_batched_transposed_a(tmm, monkeypatch):
-    monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+def test_batched_transposed_a(tmm, force):
+    force()
     run_case(tmm, 96, 80, 72, "f16", "f16", True, False, 0.25, 0.5, False, True, seed=1400, batch=3,
              what="batched TN")
 
 
-def test_one_row(tmm, monkeypatch):
+def test_one_row(tmm, force):
     """M = 1 with the full form does not take the plain GEMV kernel."""
-    monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+    force()
     run_case(tmm, 1, 4096, 4096, "bf16", "bf16", False, True, 1.0, 1.0, True, True, seed=1500, what="M=1")
 
 
-def test_beta_zero_does_not_read_c_and_empty_sum(tmm, monkeypatch):
-    monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+def test_beta_zero_does_not_read_c_and_empty_sum(tmm, force):
+    force()
     M, N, K = 70, 90, 40
     A = syn.to_bits(syn.normal((M, K), 1601), "bf16")
     B = syn.to_bits(syn.normal((N, K), 1602), "bf16")
@@ -167,23 +167,23 @@ RING_TA = [
 
 @pytest.mark.parametrize("case", RING_TA, ids=[f"{c[0]}x{c[1]}x{c[2]}-{c[3]}-{c[4]}-{'T' if c[5] else 'N'}"
                                                f"-b{c[10]}" for c in RING_TA])
-def test_transposed_a_ring(tmm, case, monkeypatch):
+def test_transposed_a_ring(tmm, case, force):
     M, N, K, fmt, out, tb, alpha, beta, relu, bias, batch = case
-    monkeypatch.setenv("TMM_FORCE_TILE", "256x256r")
+    force("256x256r")
     run_case(tmm, M, N, K, fmt, out, True, tb, alpha, beta, relu, bias, seed=1700 + M, batch=batch,
              what=f"ring TA {case}")
 
 
-def test_transposed_a_ring_integer_exact(tmm, monkeypatch):
-    monkeypatch.setenv("TMM_FORCE_TILE", "256x256r")
+def test_transposed_a_ring_integer_exact(tmm, force):
+    force("256x256r")
     for tb in (False, True):
         run_case(tmm, 264, 520, 96, "bf16", "f32", True, tb, 2.0, -1.0, True, True, seed=1800,
                  dist="int", what=f"int ring TA tb {tb}")
 
 
-def test_transposed_a_automatic_choice(tmm, monkeypatch):
+def test_transposed_a_automatic_choice(tmm, force):
     """A weight-gradient shape large enough that the ring kernel is chosen
     without forcing (2048 x 2048 outputs: 64 tiles of 256 x 256)."""
-    monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+    force()
     run_case(tmm, 2048, 2048, 128, "bf16", "f32", True, False, 1.0, 0.0, False, False, seed=1900,
              what="auto TA 2048")

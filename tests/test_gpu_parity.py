@@ -131,11 +131,11 @@ def _batched_nt(Z, M, N, K, fmt, seed):
     return A, B
 
 
-def _run_batched_nt(tmm, A, B, fmt, tile, monkeypatch):
+def _run_batched_nt(tmm, A, B, fmt, tile, force):
     if tile is None:
-        monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+        force()
     else:
-        monkeypatch.setenv("TMM_FORCE_TILE", tile)
+        force(tile)
     Z, M, K = A.shape
     N = B.shape[1]
     C = torch.full((Z, M, N), float("nan"), dtype=TORCH_DT[fmt], device=DEV)
@@ -150,31 +150,31 @@ def _run_batched_nt(tmm, A, B, fmt, tile, monkeypatch):
     (9, 512, 512, 64, "f16"),     # 36 tiles on 32 workgroups: four walk two
     (5, 768, 512, 128, "bf16"),   # 30 tiles on 24 workgroups, across batch entries
 ], ids=["f16-K128-6tiles", "bf16-K64", "f16-K64-walk", "bf16-K128-walk"])
-def test_short_k_kernel(tmm, monkeypatch, Z, M, N, K, fmt):
+def test_short_k_kernel(tmm, force, Z, M, N, K, fmt):
     """The persistent short-K kernel (forced): every batch entry against the
     oracle, and bit for bit against the two-stage kernel (same matrix
     instructions in the same K order)."""
     A, B = _batched_nt(Z, M, N, K, fmt, 61 + K)
-    C = _run_batched_nt(tmm, A, B, fmt, "shortk", monkeypatch)
+    C = _run_batched_nt(tmm, A, B, fmt, "shortk", force)
     for z in range(Z):
         o, T = oracle.gemm(fmt, A[z], B[z], trans_b=True, want_abs=True)
         check(C[z], o, T, K, what=f"short-K batch {z}")
-    ref = _run_batched_nt(tmm, A, B, fmt, "256x256s2", monkeypatch)
+    ref = _run_batched_nt(tmm, A, B, fmt, "256x256s2", force)
     assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), "short-K and two-stage kernels differ"
 
 
-def test_attention_scores_shape_takes_short_k(tmm, monkeypatch):
+def test_attention_scores_shape_takes_short_k(tmm, force):
     """Short K over many whole tiles (64 problems x 16 tiles, K = 128) is what
     the dispatch sends to the short-K kernel without forcing: the result
     equals the two-stage kernel's bit for bit, and sampled problems match the
     oracle."""
     Z, M, N, K = 64, 1024, 1024, 128
     A, B = _batched_nt(Z, M, N, K, "f16", 81)
-    C = _run_batched_nt(tmm, A, B, "f16", None, monkeypatch)
+    C = _run_batched_nt(tmm, A, B, "f16", None, force)
     for z in (0, 37, 63):
         o, T = oracle.gemm("f16", A[z], B[z], trans_b=True, want_abs=True)
         check(C[z], o, T, K, what=f"scores batch {z}")
-    ref = _run_batched_nt(tmm, A, B, "f16", "256x256s2", monkeypatch)
+    ref = _run_batched_nt(tmm, A, B, "f16", "256x256s2", force)
     assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), "short-K and two-stage kernels differ"
 
 

@@ -53,12 +53,12 @@ def operand(rows, cols, fmt, seed, pad, Z):
 
 
 @pytest.mark.parametrize("i", range(NCASE))
-def test_random_problem(tmm, i, monkeypatch):
+def test_random_problem(tmm, i, force):
     fmt, out, tb, M, N, K, pad, Z, bias, tile = draw(i)
     if tile is None:
-        monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+        force()
     else:
-        monkeypatch.setenv("TMM_FORCE_TILE", tile)
+        force(tile)
     seed = 9000 + 10 * i
     Ab, sa = operand(M, K, fmt, seed + 1, pad, Z)
     Bb, sb = operand(N, K, fmt, seed + 2, pad, Z) if tb else operand(K, N, fmt, seed + 2, pad, Z)

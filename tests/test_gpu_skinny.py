@@ -4,7 +4,7 @@ batch-size table for a 4096 x 4096 weight, plus ragged M, N and K (K tails
 that are not a multiple of the 32-element step, or of 8), padded rows, bias,
 both output widths, unaligned outputs and a batched case, all against the
 oracle.  The kernel is reached both by the automatic choice (M <= 256) and by
-TMM_FORCE_TILE=skinny."""
+the override tile=skinny (tmm_set_override)."""
 import numpy as np
 import pytest
 import torch
@@ -46,22 +46,22 @@ def _id(c):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[_id(c) for c in CASES])
-def test_skinny_parity(tmm, case, monkeypatch):
+def test_skinny_parity(tmm, case, force):
     M, N, K, fmt, out, dist, bias, pad, forced = case
     if forced:
-        monkeypatch.setenv("TMM_FORCE_TILE", "skinny")
+        force("skinny")
     else:
-        monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+        force()
     dC, o, T = gemm_case(tmm, M, N, K, fmt, out, True, dist, bias, seed=700 + 10 * CASES.index(case),
                          pad=pad)
     check(dC, o, T, K, exact=(dist == "int"), what=_id(case))
 
 
-def test_skinny_batched_and_unaligned_output(tmm, monkeypatch):
+def test_skinny_batched_and_unaligned_output(tmm, force):
     """Three problems through the strided-batched entry point, written into
     an output with a row pitch that is not a multiple of 4 elements (element
     stores) and a gap between the matrices."""
-    monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+    force()
     Z, M, N, K = 3, 12, 200, 96
     A = syn.to_bits(syn.normal((Z, M, K), 811), "bf16")
     B = syn.to_bits(syn.normal((Z, N, K), 812, 0.02), "bf16")
@@ -82,7 +82,7 @@ def test_skinny_batched_and_unaligned_output(tmm, monkeypatch):
     assert torch.isnan(Cfull.view(Z, strideC)[~keep].float()).all(), "a store landed outside C"
 
 
-def test_skinny_matches_gemv_entry(tmm, monkeypatch):
+def test_skinny_matches_gemv_entry(tmm, force):
     """M = 1 through the skinny kernel (forced) and through the GEMV kernel
     agree with the oracle on the decode shape."""
     N, K = 4096, 4096
@@ -93,9 +93,9 @@ def test_skinny_matches_gemv_entry(tmm, monkeypatch):
     dW, dx, db = on_gpu(W, "bf16"), on_gpu(x, "bf16"), torch.from_numpy(bvec).to(DEV)
     for forced in (True, False):
         if forced:
-            monkeypatch.setenv("TMM_FORCE_TILE", "skinny")
+            force("skinny")
         else:
-            monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+            force()
         y = torch.full((1, N), float("nan"), dtype=TORCH_DT["bf16"], device=DEV)
         tmm.tmm_gemm(dx, dW, y, bias=db, trans_b=True)
         torch.cuda.synchronize()
@@ -103,11 +103,10 @@ def test_skinny_matches_gemv_entry(tmm, monkeypatch):
 
 
 @pytest.mark.parametrize("tile", [f"{m}x{n}" for m in (16, 32, 64) for n in (16, 32, 64)])
-def test_every_skinny_tile(tmm, tile, monkeypatch):
+def test_every_skinny_tile(tmm, tile, force):
     """Each of the nine workgroup tiles on one ragged problem (M, N not
-    multiples of any tile, a K tail) with bias, through TMM_SKINNY_TILE."""
-    monkeypatch.setenv("TMM_FORCE_TILE", "skinny")
-    monkeypatch.setenv("TMM_SKINNY_TILE", tile)
+    multiples of any tile, a K tail) with bias, through the override skinny=<bm>x<bn>."""
+    force("skinny", skinny=tile)
     dC, o, T = gemm_case(tmm, 70, 300, 200, "bf16", "bf16", True, "normal", True, seed=900, pad=0)
     check(dC, o, T, 200, what=f"skinny tile {tile}")
 
@@ -126,24 +125,24 @@ GEMVM = [
 
 @pytest.mark.parametrize("case", GEMVM, ids=[f"M{c[0]}-N{c[1]}-K{c[2]}-{c[3]}-{c[4]}" for c in GEMVM])
 @pytest.mark.parametrize("forced", [False, True], ids=["auto", "forced"])
-def test_gemv_multi(tmm, case, forced, monkeypatch):
+def test_gemv_multi(tmm, case, forced, force):
     """A few rows through one weight (Y = X . W^T): the several-row GEMV,
-    reached automatically and through TMM_FORCE_TILE=gemvm, against the
+    reached automatically and through the override tile=gemvm, against the
     oracle."""
     M, N, K, fmt, out, bias, pad = case
     if forced:
-        monkeypatch.setenv("TMM_FORCE_TILE", "gemvm")
+        force("gemvm")
     else:
-        monkeypatch.delenv("TMM_FORCE_TILE", raising=False)
+        force()
     dC, o, T = gemm_case(tmm, M, N, K, fmt, out, True, "normal", bias, seed=950 + 10 * GEMVM.index(case),
                          pad=pad)
     check(dC, o, T, K, what=f"gemv-multi M={M} N={N} K={K}")
 
 
-def test_gemv_multi_keeps_fp16_subnormals(tmm, monkeypatch):
+def test_gemv_multi_keeps_fp16_subnormals(tmm, force):
     """fp16 subnormal activations (2^-20) against unit weights: every output
     is K * 2^-20 exactly, which a flush to zero would lose."""
-    monkeypatch.setenv("TMM_FORCE_TILE", "gemvm")
+    force("gemvm")
     M, N, K = 4, 256, 4096
     X = torch.full((M, K), 2.0 ** -20, dtype=torch.float16, device=DEV)
     W = torch.ones((N, K), dtype=torch.float16, device=DEV)

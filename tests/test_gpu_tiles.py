@@ -1,5 +1,5 @@
 """GPU parity of every tile kernel: the tile shape is pinned through
-TMM_FORCE_TILE (read by the library on each call), so the 256x256 kernels,
+the override tile=... (tmm_set_override, read by every call), so the 256x256 kernels,
 which the automatic choice only takes at large sizes, are checked against the
 oracle on small ragged problems too.  "256x256r" runs the four-stage ring
 kernel whenever K is a multiple of its 32-element step ("256x256" only for an
@@ -50,11 +50,11 @@ def _id(c):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[_id(c) for c in CASES])
-def test_every_tile(tmm, case, monkeypatch):
+def test_every_tile(tmm, case, force):
     M, N, K, fmt, out, tb, dist, bias, pad = case
     first = None
     for tile in TILES:
-        monkeypatch.setenv("TMM_FORCE_TILE", tile)
+        force(tile)
         dC, o, T, ops = gemm_case(tmm, M, N, K, fmt, out, tb, dist, bias,
                                   seed=100 + 10 * CASES.index(case), pad=pad, want_ops=True)
         check(dC, o, T, K, exact=(dist == "int"), what=f"{_id(case)} tile {tile}", f8=(fmt == "e4m3"),

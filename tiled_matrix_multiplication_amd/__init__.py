@@ -27,7 +27,7 @@ STATUS = {
 
 EXPORTS = ("tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemm_ex", "tmm_gemv", "tmm_attention_fwd",
            "tmm_conv2d_fused",
-           "tmm_status_string", "tmm_version")
+           "tmm_status_string", "tmm_version", "tmm_set_override")
 
 _DTYPE = {torch.float32: TMM_F32, torch.bfloat16: TMM_BF16, torch.float16: TMM_F16,
           torch.float8_e4m3fn: TMM_F8E4M3}
@@ -58,9 +58,10 @@ def _load() -> ctypes.CDLL:
     lib.tmm_status_string.argtypes = [ci]
     lib.tmm_status_string.restype = ctypes.c_char_p
     lib.tmm_version.argtypes = []
+    lib.tmm_set_override.argtypes = [ctypes.c_char_p]
     for f in (lib.tmm_gemm, lib.tmm_gemm_strided_batched, lib.tmm_gemm_ex, lib.tmm_gemv,
               lib.tmm_attention_fwd, lib.tmm_conv2d_fused,
-              lib.tmm_version):
+              lib.tmm_version, lib.tmm_set_override):
         f.restype = ci
     return lib
 
@@ -70,6 +71,15 @@ lib = _load()
 
 def tmm_status_string(code: int) -> str:
     return lib.tmm_status_string(int(code)).decode()
+
+
+def tmm_set_override(spec: str | None = None) -> None:
+    """Pin kernel choices for measurements and tests (keys in include/tmm.h:
+    tile=..., skinny=<bm>x<bn>, gemv=<r>x<w>); None or "" restores the
+    automatic choice."""
+    rc = lib.tmm_set_override(spec.encode() if spec else None)
+    if rc:
+        raise TmmError("tmm_set_override", rc)
 
 
 def tmm_version() -> int:

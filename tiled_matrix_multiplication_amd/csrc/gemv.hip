@@ -270,20 +270,10 @@ void launch_vec(const GemvParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((gemv_vec_kernel<WT, YT, R, WPB, false>), dim3(blocks), dim3(64 * WPB), 0, stream, p);
 }
 
-// Rows per wave and waves per workgroup of the 16-byte path.  TMM_GEMV_CFG
-// = "R,W" (R in {1,2,4}, W in {4,8,16}) pins them for measurements.
-// Read once (a function-local static is initialised once, thread-safely).
-int gemv_cfg() {
-  static const int cfg = [] {
-    const char *s = getenv("TMM_GEMV_CFG");
-    int r = 0, w = 0;
-    if (s && sscanf(s, "%d,%d", &r, &w) == 2 && (r == 1 || r == 2 || r == 4) &&
-        (w == 4 || w == 8 || w == 16))
-      return r * 100 + w;
-    return 0;
-  }();
-  return cfg;
-}
+// Rows per wave and waves per workgroup of the 16-byte path: R * 100 + W
+// from the library's override ("gemv=<R>x<W>", R in {1, 2, 4}, W in
+// {4, 8, 16}), 0 for the automatic choice.
+int gemv_cfg() { return gemv_override(); }
 
 template <int WT, int YT>
 hipError_t launch_typed(bool vec, const GemvParams &p, hipStream_t stream) {

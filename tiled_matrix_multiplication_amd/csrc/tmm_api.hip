@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "tmm.h"
@@ -35,6 +36,17 @@ int device_cu_count() {
   return cached[dev];
 }
 
+}  // namespace tmm
+
+namespace {
+uint64_t override_word();
+}
+
+namespace tmm {
+int gemv_override() {
+  const uint64_t ov = override_word();
+  return (int)((ov >> 24) & 0xff) * 100 + (int)((ov >> 32) & 0xff);
+}
 }  // namespace tmm
 
 namespace {
@@ -110,39 +122,88 @@ int check_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, cons
 
 int cu_count() { return tmm::device_cu_count(); }
 
-// TMM_FORCE_TILE = "256x256" | "256x128" | "128x128" | "256x256w4" | "256x256s2" |
-// "256x256r" | "skinny" | "generic" | "shortk" | "gemvm" pins the tile shape for measurements and tile-by-tile
-// tests ("256x256s2": 256x256 tiles on the two-stage kernel only; "256x256r":
-// on the ring kernel wherever it applies, K-contiguous B included; "skinny":
-// the skinny-M kernel wherever it applies, any M; "generic": the any-layout
-// kernel for 16-bit inputs; "shortk": the persistent short-K kernel
-// wherever it applies, any tile count; "gemvm": the several-row GEMV
-// wherever it applies; with a transposed A, "256x256" and
-// "256x256r" pick the ring kernel wherever it applies).
-// Read on every call so that a test can switch it; anything else leaves the
-// choice to pick_tile.
+// Kernel-choice override for measurements and kernel-by-kernel tests, one
+// setting for the whole library: TMM_OVERRIDE in the environment, parsed
+// once at the first call, or tmm_set_override() at run time (include/tmm.h
+// lists the keys).  Held as one packed word, so a call reads it with one
+// atomic load and a setter never leaves a half-written value.
+//   bits 0-7   tile choice + 1 (0: none): a tmm::Tile, or kOvGeneric,
+//              kOvShortK, kOvGemvMulti
+//   bits 8-15  skinny tile rows, 16-23 skinny tile columns (0: automatic)
+//   bits 24-31 GEMV rows per wave, 32-39 GEMV waves per workgroup (0: automatic)
+constexpr int kOvGeneric = 16, kOvShortK = 17, kOvGemvMulti = 18;
+constexpr uint64_t kOvSet = 1ull << 63;
+
+std::atomic<uint64_t> g_override{0};
+std::once_flag g_override_env;
+
+bool parse_override(const char *spec, uint64_t *out) {
+  uint64_t v = kOvSet;
+  if (!spec) {
+    *out = v;
+    return true;
+  }
+  char buf[256];
+  if (strlen(spec) >= sizeof buf) return false;
+  strcpy(buf, spec);
+  char *save = nullptr;
+  for (char *tok = strtok_r(buf, "; ", &save); tok; tok = strtok_r(nullptr, "; ", &save)) {
+    char *eq = strchr(tok, '=');
+    if (!eq) return false;
+    *eq = 0;
+    const char *key = tok, *val = eq + 1;
+    if (!strcmp(key, "tile")) {
+      static const struct { const char *name; int code; } names[] = {
+          {"256x256", tmm::kTile256x256}, {"256x128", tmm::kTile256x128},
+          {"128x128", tmm::kTile128x128}, {"256x256w4", tmm::kTile256x256w4},
+          {"256x256s2", tmm::kTile256x256s2}, {"256x256r", tmm::kTile256x256r},
+          {"skinny", tmm::kTileSkinny}, {"generic", kOvGeneric}, {"shortk", kOvShortK},
+          {"gemvm", kOvGemvMulti}};
+      int code = -1;
+      for (const auto &n : names)
+        if (!strcmp(val, n.name)) code = n.code;
+      if (code < 0) return false;
+      v = (v & ~0xffull) | (uint64_t)(code + 1);
+    } else if (!strcmp(key, "skinny")) {
+      int m = 0, n = 0;
+      if (sscanf(val, "%dx%d", &m, &n) != 2 || (m != 16 && m != 32 && m != 64) ||
+          (n != 16 && n != 32 && n != 64))
+        return false;
+      v = (v & ~(0xffffull << 8)) | ((uint64_t)m << 8) | ((uint64_t)n << 16);
+    } else if (!strcmp(key, "gemv")) {
+      int r = 0, w = 0;
+      if (sscanf(val, "%dx%d", &r, &w) != 2 || (r != 1 && r != 2 && r != 4) ||
+          (w != 4 && w != 8 && w != 16))
+        return false;
+      v = (v & ~(0xffffull << 24)) | ((uint64_t)r << 24) | ((uint64_t)w << 32);
+    } else {
+      return false;
+    }
+  }
+  *out = v;
+  return true;
+}
+
+uint64_t override_word() {
+  std::call_once(g_override_env, [] {
+    uint64_t v = kOvSet;
+    if (!parse_override(getenv("TMM_OVERRIDE"), &v)) v = kOvSet;  // a bad value pins nothing
+    uint64_t expect = 0;
+    g_override.compare_exchange_strong(expect, v);
+  });
+  return g_override.load(std::memory_order_acquire);
+}
+
+int override_tile_code() { return (int)(override_word() & 0xff) - 1; }
+
+// A pinned tmm::Tile shape, or -1.
 int forced_tile() {
-  const char *s = getenv("TMM_FORCE_TILE");
-  if (!s) return -1;
-  if (!strcmp(s, "256x256")) return tmm::kTile256x256;
-  if (!strcmp(s, "256x128")) return tmm::kTile256x128;
-  if (!strcmp(s, "128x128")) return tmm::kTile128x128;
-  if (!strcmp(s, "256x256w4")) return tmm::kTile256x256w4;
-  if (!strcmp(s, "256x256s2")) return tmm::kTile256x256s2;
-  if (!strcmp(s, "256x256r")) return tmm::kTile256x256r;
-  if (!strcmp(s, "skinny")) return tmm::kTileSkinny;
-  return -1;
+  const int c = override_tile_code();
+  return c >= 0 && c < kOvGeneric ? c : -1;
 }
-
-bool forced_short_k() {
-  const char *s = getenv("TMM_FORCE_TILE");
-  return s && !strcmp(s, "shortk");
-}
-
-bool forced_gemv_multi() {
-  const char *s = getenv("TMM_FORCE_TILE");
-  return s && !strcmp(s, "gemvm");
-}
+bool forced_generic() { return override_tile_code() == kOvGeneric; }
+bool forced_short_k() { return override_tile_code() == kOvShortK; }
+bool forced_gemv_multi() { return override_tile_code() == kOvGemvMulti; }
 
 // Largest M for which the several-row GEMV is chosen automatically: W 4096 x
 // 4096 fp16 + bias, graph-timed, against the skinny MFMA kernel: M = 2
@@ -159,16 +220,12 @@ constexpr int64_t kSkinnyMaxM = 256;
 // K, i.e. K (M ceil(N/bn) + N ceil(M/bm)) elements -- among the shapes that
 // give every CU a tile (the most tiles if none does).
 void pick_skinny(int64_t M, int64_t N, int64_t batch, int *bm, int *bn) {
-  // TMM_SKINNY_TILE = "<bm>x<bn>" (each 16, 32 or 64) pins the tile for
-  // measurements.
-  if (const char *e = getenv("TMM_SKINNY_TILE")) {
-    int m = 0, n = 0;
-    if (sscanf(e, "%dx%d", &m, &n) == 2 && (m == 16 || m == 32 || m == 64) &&
-        (n == 16 || n == 32 || n == 64)) {
-      *bm = m;
-      *bn = n;
-      return;
-    }
+  // the override's "skinny=<bm>x<bn>" pins the tile
+  const uint64_t ov = override_word();
+  if ((ov >> 8) & 0xff) {
+    *bm = (int)((ov >> 8) & 0xff);
+    *bn = (int)((ov >> 16) & 0xff);
+    return;
   }
   const int64_t cus = cu_count();
   double best = 1e300;
@@ -233,8 +290,7 @@ tmm::Tile pick_tile(int64_t M, int64_t N, int64_t batch, int ab) {
 bool use_ring_ta(int64_t M, int64_t N, int64_t batch) {
   const int f = forced_tile();
   if (f == tmm::kTile256x256 || f == tmm::kTile256x256r) return true;
-  const char *s = getenv("TMM_FORCE_TILE");
-  if (s && !strcmp(s, "generic")) return false;
+  if (forced_generic()) return false;
   const int cus = cu_count();
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256) * batch;
   const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64) * batch;
@@ -324,10 +380,7 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
                      (trans_b || (N * e) % 16 == 0);
     const int f = forced_tile();
     const bool skinny_ok = vec && trans_b && (ab == TMM_BF16 || ab == TMM_F16);
-    const bool generic_forced = [] {
-      const char *s = getenv("TMM_FORCE_TILE");
-      return s && !strcmp(s, "generic");
-    }();
+    const bool generic_forced = forced_generic();
     // Rows that are not 16-byte aligned (K or N not a multiple of 8 16-bit
     // elements, e.g. 1000 x 3000 x 777) leave the tiled kernels on word
     // loads over 128 x 128 tiles.  With an N-contiguous B the any-layout
@@ -518,5 +571,13 @@ const char *tmm_status_string(int status) {
 }
 
 int tmm_version(void) { return kVersion; }
+
+int tmm_set_override(const char *spec) {
+  uint64_t v = 0;
+  if (!parse_override(spec, &v)) return TMM_ERR_ARG;
+  override_word();  // the environment's value is read first, then replaced
+  g_override.store(v, std::memory_order_release);
+  return TMM_OK;
+}
 
 }  // extern "C"

@@ -10,6 +10,9 @@ namespace tmm {
 // Compute units of the current device (cached per device, thread-safe).
 int device_cu_count();
 
+// GEMV launch shape pinned by the library's override (R * 100 + W), or 0.
+int gemv_override();
+
 // Element formats, same numbering as tmm_dtype in include/tmm.h.
 enum Fmt : int { kF32 = 0, kBF16 = 1, kF16 = 2, kF8 = 3 };
 
