@@ -827,15 +827,30 @@ template <int AB, int CT, bool NT, int NW>
 hipError_t launch_ring(const GemmParams &p, hipStream_t stream);
 
 template <int AB, int CT, bool NT>
+hipError_t launch_quad(const GemmParams &p, hipStream_t stream);
+
+template <int AB, int CT, bool NT>
 hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t stream) {
   if (vec) {
     switch (tile) {
       case kTile256x256:
+      case kTile256x256q:
+        // Four-wave kernel (gemm_quad.h): 16-bit inputs, an even number (at
+        // least 4) of 32-element K-steps, the plain form.  Chosen for every
+        // such 256x256 tile: it measured faster than the ring and two-stage
+        // kernels at every shape timed (4096^3 NN fp32 out 118.1 -> 102.3 us;
+        // 8192x12288x4096 NT 661.6 -> 621.5 us; 8192^3 NN 880 -> 765 us).
+        if constexpr (AB == kBF16 || AB == kF16) {
+          if (p.K % 64 == 0 && p.K >= 128 && p.beta == 0.f && p.act == 0)
+            return launch_quad<AB, CT, NT>(p, stream);
+        }
+        [[fallthrough]];
       case kTile256x256r:
         // Four-stage ring kernel (gemm_ring.h) for 16-bit and fp8 inputs and
         // whole 64-byte K-steps; chosen automatically for fp8, and for 16-bit
-        // inputs with an N-contiguous B, where it measured faster (with a
-        // K-contiguous 16-bit B the two-stage kernel was).
+        // inputs with an N-contiguous B when the four-wave kernel does not
+        // apply (with a K-contiguous 16-bit B the two-stage kernel measured
+        // faster).
         if constexpr (AB != kF32) {
           if (p.K % (64 / FmtBytes<AB>::value) == 0 &&
               (tile == kTile256x256r || !NT || AB == kF8))

@@ -1,0 +1,335 @@
+// Tiled GEMM on gfx950 matrix cores with four waves per 256x256 tile, each
+// wave owning a 128x128 block of C: the kernel for 16-bit inputs whose rows
+// are 16-byte aligned and whose K is a multiple of 64, at least 128.
+//
+//   C[z] = scale * A[z] . op(B[z]) (+ bias),  row-major, z < batch
+//
+// It keeps the four-stage LDS ring of gemm_ring.h (same stage size, same
+// direct 16-byte global->LDS loads issued three K-steps ahead, same
+// barrier-per-step protocol) and changes what runs on it, for two measured
+// properties of the chip:
+//   * LDS read bandwidth is the loop's limit with eight 128x64 waves: per
+//     32-element K-step a CU reads 64 KiB of A fragments (each A row block
+//     is read by the four waves sharing it) and 32 KiB of transposed B
+//     fragments against 1024 matrix-core cycles per SIMD, at ~150 B/clk
+//     (16-byte reads) and ~111 B/clk (transposing reads) per CU.  With four
+//     waves of 128x128 each A block is read by two waves and each B block by
+//     two: 32 KiB + 32 KiB, a third less.  That is the register blocking of
+//     the Lecture 27 notes (section 2.4) taken to the largest block a wave
+//     can hold: 256 fp32 accumulators per lane, kept in the accumulation
+//     registers (AGPRs), with the fragments in the 256 architectural ones.
+//   * Under random data the matrix cores run at the chip's power limit, and
+//     the 16x16x32 instruction sustains a higher clock than the 32x32x16 one
+//     for the same work (0.745 vs 0.68 of the dense peak in a register-only
+//     loop on N(0,1) bf16 operands): it touches its accumulators once per 32
+//     K instead of once per 16.  So each wave computes 8x8 blocks of 16x16.
+// Fragments: lane l of a 16x16x32 block holds row (A) or column (B) l % 16
+// and K elements 8 (l / 16) .. +7 of the step.
+//   * A, and a K-contiguous B (trans_b): 16-byte reads of the stage's 64-byte
+//     rows (chunk c of row r at c ^ ((r >> 2) & 3): the 16 rows one 16-lane
+//     group reads fall on 16 distinct bank groups).
+//   * an N-contiguous B (NN): the stage holds k-rows of 256 elements as in
+//     memory; the transposing read ds_read_b64_tr_b16 hands lane i of a
+//     16-lane group the 4 elements (i mod 4) of the 8-byte pieces addressed
+//     by lanes 4e + i / 4, so with lane s pointing at k-row k0 + s / 4,
+//     columns n0 + 4 (s mod 4) .. +3, lane i receives B[k0 .. k0+3][n0 + i];
+//     two such reads (k0 and k0 + 4) make a fragment.  The 32 lanes served
+//     together read 8 k-rows (two groups of 4, 8 apart) x 32 bytes, so chunk
+//     c of k-row r sits at c ^ (2 (r mod 4) + 8 ((r / 8) mod 2)): 16 distinct
+//     positions among the 16 chunk slots of a 256-byte bank row.
+// Within a step a wave issues its 64 matrix instructions row block by row
+// block; after a row block's instructions it reads the next step's A
+// fragment of that row block into the same registers, and between them the
+// next step's B fragments (into a second set) and one of its eight direct
+// loads, in an order fixed by scheduling fences.
+#pragma once
+
+#include <type_traits>
+
+#include "gemm_mfma.h"
+#include "gemm_ring.h"
+
+namespace tmm {
+namespace gemm_detail {
+
+// s_waitcnt immediate waiting for vmcnt <= n only (lgkmcnt and expcnt at
+// their maximum): a step's own LDS reads need not have landed at the
+// barrier, only the direct loads that publish the next stage.
+constexpr int vm_only_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// NN B stage for 16-wide fragments: 16-byte chunk c of k-row r at c ^ qswz(r).
+__device__ __forceinline__ int qswz(int r) { return 2 * (r & 3) + 8 * ((r >> 3) & 1); }
+
+template <int AB>
+__device__ __forceinline__ f32x4 mma16(const i32x4 &a, const i32x4 &b, const f32x4 &c) {
+  if constexpr (AB == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Epilogue of a wave's 128x128 block held as 8x8 16x16 accumulators (lane l:
+// column 16 j + l % 16, rows 16 i + 4 (l / 16) + r): in 32-row bands through
+// the wave's LDS area `st` (rows kQuadPitch bytes apart, 16 bytes of padding
+// so the four 16-lane groups of a write land 16 banks apart) as finished
+// values (scale, bias, one nearest-even rounding), then back 16 bytes per
+// lane along the rows and out with whole-row stores, masked by M and N.
+template <int CT>
+constexpr int quad_pitch() { return 128 * FmtBytes<CT>::value + 16; }
+
+template <int CT>
+__device__ __forceinline__ void store_quad(const f32x4 (&acc)[8][8], char *st, char *C, int64_t ldc,
+                                           int64_t M, int64_t N, int64_t row0, int64_t col0,
+                                           const float *bias, float scale, int lane) {
+  constexpr int CE = FmtBytes<CT>::value;
+  constexpr int P = quad_pitch<CT>();
+  constexpr int CPR = 128 * CE / 16;        // 16-byte pieces per row
+  constexpr int EPC = 16 / CE;              // elements per piece
+  constexpr int NRD = 32 * CPR / 64;        // read instructions per band
+  const int c16 = lane & 15, g = lane >> 4;
+  const bool vec = ((uintptr_t)C % 16) == 0 && ((ldc * CE) % 16) == 0;
+  float bv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t col = col0 + 16 * j + c16;
+    bv[j] = (bias && col < N) ? bias[col] : 0.f;
+  }
+#pragma unroll
+  for (int band = 0; band < 4; ++band) {
+    if (row0 + 32 * band >= M) break;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * ii + 4 * g + r;
+          const uint32_t b = out_bits<CT>(acc[2 * band + ii][j][r] * scale + bv[j]);
+          char *d = st + row * P + (16 * j + c16) * CE;
+          if constexpr (CE == 4) *(uint32_t *)d = b;
+          else *(uint16_t *)d = (uint16_t)b;
+        }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < NRD; ++t) {
+      const int c = t * 64 + lane;
+      const int row = c / CPR, pc = c % CPR;
+      const i32x4 v = *(const i32x4 *)(st + row * P + pc * 16);
+      const int64_t grow = row0 + 32 * band + row;
+      const int64_t gcol = col0 + (int64_t)pc * EPC;
+      if (grow >= M || gcol >= N) continue;
+      char *dst = C + (grow * ldc + gcol) * CE;
+      if (vec && gcol + EPC <= N) {
+        __builtin_nontemporal_store(v, (i32x4 *)dst);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          if (gcol + e < N) {
+            const uint32_t w = (uint32_t)v[(e * CE) / 4];
+            if constexpr (CE == 4) ((uint32_t *)dst)[e] = w;
+            else ((uint16_t *)dst)[e] = (uint16_t)(w >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next band's writes
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int AB, int CT, bool NT>
+__global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 256, NW = 4;
+  constexpr int E = FmtBytes<AB>::value;
+  constexpr int CE = FmtBytes<CT>::value;
+  constexpr int ROWB = kRingRowBytes;           // 64 bytes of K per tile row per step
+  constexpr int BK = ROWB / E;                  // 32
+  constexpr int A_BYTES = BM * ROWB;            // 16 KiB
+  constexpr int B_BYTES = BN * ROWB;            // 16 KiB
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int S = kRingStages;                // 4
+  constexpr int NB_ROW = BN * E;                // NN: bytes of one k-row of the B stage
+  constexpr int LA = A_BYTES / 1024 / NW;       // 4 direct loads per wave per step (A)
+  constexpr int LB = B_BYTES / 1024 / NW;       // 4 (B)
+  constexpr int LPS = LA + LB;
+  static_assert(E == 2, "four-wave kernel: 16-bit inputs");
+  static_assert(S == 4 && BK == 32 && NB_ROW == 512, "geometry");
+
+  __shared__ __attribute__((aligned(16))) char lds[S * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  int64_t pid = remap_xcd(blockIdx.x, (int64_t)gridDim.x);
+  const int64_t z = pid / tiles;
+  pid -= z * tiles;
+  int64_t tm, tn;
+  group_order(pid, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  const char *A = (const char *)p.A + z * p.strideA * E;
+  const char *B = (const char *)p.B + z * p.strideB * E;
+
+  // ---- direct-load sources (byte offsets < 4 GiB, checked by the host).
+  // A and an NT B: instruction i of wave w fills stage rows 64 w + 16 i ..+15;
+  // lane L lands at row L / 4, position L % 4 and loads logical chunk
+  // (L % 4) ^ swz64(row).  Rows past M (N) read the last valid row.
+  uint32_t a_off[LA], b_off[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int row = wave * (BM / NW) + i * 16 + (lane >> 2);
+    const int64_t r = min64(m0 + row, M - 1);
+    a_off[i] = (uint32_t)(r * p.lda * E + (((lane & 3) ^ swz64(row)) << 4));
+  }
+  if constexpr (NT) {
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int row = wave * (BN / NW) + i * 16 + (lane >> 2);
+      const int64_t r = min64(n0 + row, N - 1);
+      b_off[i] = (uint32_t)(r * p.ldb * E + (((lane & 3) ^ swz64(row)) << 4));
+    }
+  } else {
+    // NN: instruction i of wave w fills k-rows 8 w + 2 i, +1; lane L lands at
+    // k-row L / 32, position L % 32 and loads logical chunk (L % 32) ^
+    // qswz(row).  A chunk wholly past N (the host ensures N * E % 16 == 0)
+    // reads chunk 0 of the tile; it only feeds outputs that are not stored.
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int row = wave * (BK / NW) + i * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ qswz(row);
+      const int64_t col = n0 + (int64_t)c * (16 / E);
+      const int64_t ccol = col < N ? col : n0;
+      b_off[i] = (uint32_t)(((int64_t)row * p.ldb + ccol) * E);
+    }
+  }
+  const int64_t kstep_b = NT ? (int64_t)ROWB : (int64_t)BK * p.ldb * E;
+  const uint32_t lds0 = lds_addr(lds);
+
+  // ---- fragment addresses (bytes within a stage)
+  const int l16 = lane & 15, G = lane >> 4;
+  // A (and NT B): row block base + lane row l16, chunk G (swizzled)
+  const int a_lane = l16 * ROWB + ((G ^ ((l16 >> 2) & 3)) << 4);
+  const int a_base = wm * 128 * ROWB + a_lane;                   // + 1024 i
+  const int bt_base = A_BYTES + wn * 128 * ROWB + a_lane;        // NT: + 1024 j
+  // NN: lane (G, s = l16) reads k-row 8 G + 4 h + s / 4, columns
+  // 128 wn + 16 j + 4 (s % 4) .. +3; see the header comment for the swizzle.
+  // The block index j only flips the 16 * qswz field: address = base ^ 32 j.
+  const int f = 2 * (l16 >> 2) + 8 * (G & 1);
+  const int bn_base = A_BYTES + (8 * G + (l16 >> 2)) * NB_ROW + 256 * wn + 16 * ((l16 & 3) >> 1) +
+                      8 * (l16 & 1) + 16 * f;
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  i32x4 fa[8];
+  i32x4 fb0[8], fb1[8];
+
+  auto issue_one = [&](int64_t kt, int stage, int q) __attribute__((always_inline)) {
+    const uint32_t la = lds0 + (uint32_t)(stage * STAGE);
+    if (q < LA) {
+      dma16(A + kt * ROWB + a_off[q], la + (wave * (BM / NW) + q * 16) * ROWB);
+    } else {
+      const int i = q - LA;
+      if constexpr (NT)
+        dma16(B + kt * kstep_b + b_off[i], la + A_BYTES + (wave * (BN / NW) + i * 16) * ROWB);
+      else
+        dma16(B + kt * kstep_b + b_off[i], la + A_BYTES + (wave * (BK / NW) + i * 2) * NB_ROW);
+    }
+  };
+  auto read_a = [&](int stage, int i) __attribute__((always_inline)) {
+    fa[i] = *(const i32x4 *)(lds + stage * STAGE + a_base + i * 16 * ROWB);
+  };
+  auto read_b = [&](int stage, i32x4 (&fb)[8], int j) __attribute__((always_inline)) {
+    if constexpr (NT) {
+      fb[j] = *(const i32x4 *)(lds + stage * STAGE + bt_base + j * 16 * ROWB);
+    } else {
+      const char *pb = lds + stage * STAGE + (bn_base ^ (32 * j));
+      const i32x2 lo = __builtin_bit_cast(i32x2, lds_read_tr16(pb));
+      const i32x2 hi = __builtin_bit_cast(i32x2, lds_read_tr16(pb + 4 * NB_ROW));
+      fb[j] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+
+  const int64_t nsteps = K / BK;  // the host guarantees K % (2 BK) == 0, K >= 4 BK
+  constexpr int D = S - 1;        // steps loaded ahead
+  auto stage_of = [](int64_t k) { return (int)(k & (S - 1)); };
+  const int64_t pro = min64(D, nsteps);
+  for (int64_t k = 0; k < pro; ++k)
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) issue_one(k, (int)k, q);
+  // steps 0 and 1 landed (step 2 may still be in flight), then published
+  if (pro > 2) __builtin_amdgcn_s_waitcnt(vm_wait(LPS));
+  else __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) read_a(0, i);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) read_b(0, fb0, j);
+
+  // Step kt: matrix instructions from fa / cb; the next step's fragments into
+  // fa (row block by row block, after its last use) and nb -- on the last
+  // step a harmless read of a stale stage; with LOAD, step kt + 3's direct
+  // loads into the stage step kt - 1 used.  Barrier b(kt) then publishes
+  // step kt + 2 (its loads are waited for first; step kt + 3's stay in
+  // flight).  No vector register depends on a branch: the loop runs the
+  // steps that load, the last three are written out after it.
+  auto step = [&](int64_t kt, const i32x4 (&cb)[8], i32x4 (&nb)[8], auto load_tag)
+      __attribute__((always_inline)) {
+    constexpr bool LOAD = decltype(load_tag)::value;
+    const int nxt = stage_of(kt + 1);
+    const int lst = stage_of(kt + D);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[i][j] = mma16<AB>(fa[i], cb[j], acc[i][j]);
+        if (j == 1) read_b(nxt, nb, i);
+        if (LOAD && j == 3) issue_one(kt + D, lst, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      read_a(nxt, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(vm_only_wait(LOAD ? LPS : 0));
+    __builtin_amdgcn_s_barrier();
+  };
+  using Load = std::integral_constant<bool, true>;
+  using NoLoad = std::integral_constant<bool, false>;
+  // nsteps is even and >= 4 (the host sends other K elsewhere)
+  int64_t kt = 0;
+  for (; kt + 4 < nsteps; kt += 2) {
+    step(kt, fb0, fb1, Load());
+    step(kt + 1, fb1, fb0, Load());
+  }
+  step(kt, fb0, fb1, Load());
+  step(kt + 1, fb1, fb0, NoLoad());
+  step(kt + 2, fb0, fb1, NoLoad());
+  step(kt + 3, fb1, fb0, NoLoad());
+
+  // ---- epilogue (the loop's last barrier follows every LDS read of the stages)
+  static_assert(NW * 32 * quad_pitch<CT>() <= S * STAGE, "epilogue staging");
+  char *C = (char *)p.C + z * p.strideC * CE;
+  store_quad<CT>(acc, lds + wave * 32 * quad_pitch<CT>(), C, p.ldc, M, N, m0 + wm * 128, n0 + wn * 128,
+                 p.bias, p.scale, lane);
+}
+
+template <int AB, int CT, bool NT>
+hipError_t launch_quad(const GemmParams &p, hipStream_t stream) {
+  const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
+  hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace gemm_detail
+}  // namespace tmm

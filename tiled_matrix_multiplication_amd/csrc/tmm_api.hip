@@ -157,6 +157,7 @@ bool parse_override(const char *spec, uint64_t *out) {
           {"256x256", tmm::kTile256x256}, {"256x128", tmm::kTile256x128},
           {"128x128", tmm::kTile128x128}, {"256x256w4", tmm::kTile256x256w4},
           {"256x256s2", tmm::kTile256x256s2}, {"256x256r", tmm::kTile256x256r},
+          {"256x256q", tmm::kTile256x256q},
           {"skinny", tmm::kTileSkinny}, {"generic", kOvGeneric}, {"shortk", kOvShortK},
           {"gemvm", kOvGemvMulti}};
       int code = -1;

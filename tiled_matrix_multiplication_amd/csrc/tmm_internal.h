@@ -27,6 +27,7 @@ enum Tile : int {
   kTile256x256s2 = 4,  // 256x256 on the two-stage kernel only
   kTile256x256r = 5,   // 256x256 on the ring kernel wherever it applies (also trans_b)
   kTileSkinny = 6,     // the skinny-M kernel (16-bit NT only); chosen in the dispatch
+  kTile256x256q = 7,   // 256x256 on the four-wave 128x128-per-wave kernel (16-bit inputs)
   kNumAutoTiles = 3
 };
 
@@ -48,7 +49,8 @@ struct GemmParams {
 // Rows/columns of a workgroup tile.
 inline int tile_bm(Tile t) { return t == kTile128x128 ? 128 : 256; }
 inline int tile_bn(Tile t) {
-  return (t == kTile256x256 || t == kTile256x256w4 || t == kTile256x256s2 || t == kTile256x256r)
+  return (t == kTile256x256 || t == kTile256x256w4 || t == kTile256x256s2 || t == kTile256x256r ||
+          t == kTile256x256q)
              ? 256
              : 128;
 }
