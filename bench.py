@@ -430,6 +430,66 @@ def gpu_state_under_load(run, seconds=1.0):
             "source": "amdsmi GPU metrics (in process), read once while the timed kernel ran back to back"}
 
 
+def read_ceiling(rows=4096, row_bytes=8192, copies=18, waves=(4, 8, 16)):
+    """The GEMV's weight stream alone (include/tmm_probes.h, tmmp_stream_read):
+    W's bytes read once with the GEMV's launch shape and access pattern and
+    no arithmetic, over `copies` rotated buffers, timed like the GEMV (launches
+    in a HIP graph).  For each waves-per-workgroup setting: microseconds per
+    launch and GB/s; the best is the measured ceiling the GEMV is set against."""
+    import torch
+
+    import synthetic as syn
+    import tiled_matrix_multiplication_amd.probes as probes
+    n = rows * row_bytes // 2
+    base = syn.as_torch(syn.to_bits(syn.normal((rows, row_bytes // 2), 7001, 0.02), "bf16"), "bf16").to("cuda:0")
+    bufs = [base.clone().view(-1) for _ in range(copies)]
+    assert bufs[0].numel() == n
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    out = {}
+    for w in waves:
+        def run(i, w=w):
+            probes.stream_read(bufs[i % copies], rows, row_bytes, w, sink)
+        ms = time_graph(run, GRAPH_LAUNCHES, 5, 20)
+        out[w] = {"us_per_launch": round(ms * 1e3, 3), "GB/s": round(rows * row_bytes / (ms * 1e-3) / 1e9, 1)}
+    best = min(out, key=lambda w: out[w]["us_per_launch"])
+    del bufs, base
+    return {"bytes_per_launch": rows * row_bytes, "copies_rotated": copies,
+            "timing": f"{GRAPH_LAUNCHES} launches captured in one HIP graph, replayed",
+            "by_waves_per_group": {str(w): out[w] for w in waves}, "best_waves_per_group": best,
+            "us_per_launch": out[best]["us_per_launch"], "achieved": out[best]["GB/s"], "unit": "GB/s",
+            "frac_of_peak": round(out[best]["GB/s"] / PEAK_HBM_GBS, 4)}
+
+
+def mfma_ceiling(flops=2.0 * 4096 ** 3):
+    """The matrix cores alone (include/tmm_probes.h, tmmp_mfma_loop): the
+    headline's flops as bf16 matrix instructions on register-resident
+    N(0,1) operands (no loads, no LDS, no stores), 256 workgroups of 8 waves,
+    for both instruction shapes.  Random operands draw more power than zeros,
+    and the chip lowers its clock to stay within its power limit, so this is
+    the rate a GEMM on such data can approach, below the published peak."""
+    import torch
+
+    import tiled_matrix_multiplication_amd.probes as probes
+    groups = 256
+    iters = int(round(flops / (groups * 8 * (1 << 20))))
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(7002)
+    ops = torch.randn(1 << 25, device="cuda:0", generator=g).to(torch.bfloat16)
+    zeros = torch.zeros_like(ops)
+    sink = torch.empty(groups * 512, dtype=torch.float32, device="cuda:0")
+    out = {}
+    for label, data in (("random", ops), ("zeros", zeros)):
+        for shape, name in ((1, "16x16x32"), (0, "32x32x16")):
+            def run(i, shape=shape, data=data):
+                probes.mfma_loop(data, shape, groups, iters, sink)
+            ms, _ = time_steps(run, 50, 5)
+            tf = groups * 8 * iters * (1 << 20) / (ms * 1e-3) / 1e12
+            out[f"{label}_{name}"] = {"us_per_launch": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+                                      "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+    del ops, zeros
+    return out
+
+
 def copies_for(name):
     """Enough distinct input copies that a launch finds its operands out of the MALL."""
     M, N, K, Z, fin, fout, tb, bias = WORKLOADS[name]
@@ -492,8 +552,8 @@ CSRC = os.path.join(ROOT, "tiled_matrix_multiplication_amd", "csrc")
 # Sources that define each workload's dominant kernel (the host dispatch and
 # the shared parameter header are not part of it).
 KERNEL_SOURCES = {
-    "gemm": ["gemm_mfma.h", "gemm_ring.h", "gemm_f32.hip", "gemm_bf16.hip", "gemm_f16.hip", "gemm_f8.hip",
-             "gemm_ring_ta.hip", "gemm_short_k.hip"],
+    "gemm": ["gemm_mfma.h", "gemm_ring.h", "gemm_quad.h", "load_words.h", "gemm_f32.hip", "gemm_bf16.hip",
+             "gemm_f16.hip", "gemm_f8.hip", "gemm_ring_ta.hip", "gemm_short_k.hip"],
     "gemv": ["gemv.hip"],
     "skinny": ["gemm_skinny.hip"],
     "attention": ["attention.hip"],
@@ -793,6 +853,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="square_bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-gemv", action="store_true", help="skip the GEMV side measurement")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured ceilings (matrix cores alone, the GEMV's read stream alone)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES, --steps times (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -862,6 +924,16 @@ def main(argv=None):
         del g
     if name == "square_bf16":
         line["gpu_state"] = gpu_state_under_load(launcher(name, r["sets"], None, 1.0, 1.0))
+    if name == "square_bf16" and not args.no_ceilings:
+        c = mfma_ceiling()
+        best = max(v["TFLOP/s"] for k, v in c.items() if k.startswith("random"))
+        line["mfma_ceiling"] = dict(c, note="bf16 matrix instructions alone on register-resident operands, the "
+                                            "headline's flops; the chip's clock falls under random data",
+                                    headline_frac_of_random_ceiling=round(value / best, 4))
+        if "gemv" in line:
+            rc = read_ceiling()
+            line["gemv"]["read_ceiling"] = rc
+            line["gemv"]["frac_of_read_ceiling"] = round(line["gemv"]["achieved"] / rc["achieved"], 4)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(name, r)
     line["wall_s_timed"] = round(r["wall"], 4)

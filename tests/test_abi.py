@@ -245,3 +245,34 @@ def test_override_accepts_the_documented_keys_and_rejects_others(tmm):
         assert tmm.lib.tmm_set_override(None) == 0
     finally:
         tmm.tmm_set_override(None)
+
+
+PROBES_HEADER = os.path.join(ROOT, "include", "tmm_probes.h")
+
+
+def test_probe_library_exports_its_header():
+    """libtmm_probes.so (measurement kernels) exports what include/tmm_probes.h declares."""
+    import tiled_matrix_multiplication_amd.probes as probes
+    text = re.sub(r"/\*.*?\*/", "", open(PROBES_HEADER).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(tmmp_[a-z0-9_]+)\s*\(", text)))
+    assert declared == sorted(probes.EXPORTS)
+    raw = ctypes.CDLL(probes.LIB_PATH)
+    for name in declared:
+        assert hasattr(raw, name), name
+
+
+def test_probe_arguments_checked_on_host():
+    import tiled_matrix_multiplication_amd.probes as probes
+    lib = probes.lib
+    sink = ctypes.c_void_p(0x400000)
+    assert lib.tmmp_stream_read(FAKE, 4, 1000, 16, sink, None) == -1       # row bytes not a multiple of 1 KiB
+    assert lib.tmmp_stream_read(FAKE, 4, 3072, 16, sink, None) == -1       # not a power of two KiB
+    assert lib.tmmp_stream_read(FAKE, 4, 8192, 3, sink, None) == -9        # waves per group
+    assert lib.tmmp_stream_read(None, 4, 8192, 16, sink, None) == -3
+    assert lib.tmmp_stream_read(ctypes.c_void_p(0x100004), 4, 8192, 16, sink, None) == -7
+    assert lib.tmmp_stream_read(FAKE, 0, 8192, 16, sink, None) == 0       # nothing to read
+    assert lib.tmmp_mfma_loop(FAKE, 1 << 20, 1, 256, 64, sink, None) == -1  # operands under 16 MiB
+    assert lib.tmmp_mfma_loop(FAKE, 1 << 24, 2, 256, 64, sink, None) == -9  # shape
+    assert lib.tmmp_mfma_loop(None, 1 << 24, 1, 4, 64, sink, None) == -3
+    assert lib.tmmp_mfma_loop(FAKE, 1 << 24, 1, 256, 64, sink, None) == -1  # 256 groups need 48 MiB
+    assert lib.tmmp_mfma_loop(FAKE, 1 << 24, 1, 0, 64, sink, None) == 0

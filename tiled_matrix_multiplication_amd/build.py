@@ -1,7 +1,8 @@
 """Build libtmm.so in-tree with hipcc for gfx950.
 
 Each csrc/*.hip file is compiled to an object under _build/ (in parallel),
-then linked into tiled_matrix_multiplication_amd/libtmm.so.  Run as
+then linked into tiled_matrix_multiplication_amd/libtmm.so; the measurement
+kernels under probes/ become libtmm_probes.so.  Run as
 ``python tiled_matrix_multiplication_amd/build.py`` (not through the package,
 whose import loads the library this script replaces).
 """
@@ -18,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtmm.so")
+PROBES = os.path.join(PKG, "probes")
+PROBE_LIB = os.path.join(PKG, "libtmm_probes.so")
 ARCH = "gfx950"
 
 CXXFLAGS = [
@@ -64,7 +67,22 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probes(hipcc, verbose)
     return LIB
+
+
+def build_probes(hipcc: str, verbose: bool = False) -> str:
+    """The measurement kernels (include/tmm_probes.h) as libtmm_probes.so."""
+    srcs = sorted(os.path.join(PROBES, f) for f in os.listdir(PROBES) if f.endswith(".hip"))
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc, *CXXFLAGS, "-shared", *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the probes:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

@@ -40,8 +40,10 @@
 // Within a step a wave issues its 64 matrix instructions row block by row
 // block; after a row block's instructions it reads the next step's A
 // fragment of that row block into the same registers, and between them the
-// next step's B fragments (into a second set) and one of its eight direct
-// loads, in an order fixed by scheduling fences.
+// two halves of one of the next step's B fragments (into a second set, after
+// the second and fifth instruction) and one of its eight direct loads (after
+// the seventh), in an order fixed by scheduling fences.  (Other placements
+// measured within 2 %; all eight loads in the first row block, 5-9 % slower.)
 #pragma once
 
 #include <type_traits>
@@ -250,14 +252,20 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   auto read_a = [&](int stage, int i) __attribute__((always_inline)) {
     fa[i] = *(const i32x4 *)(lds + stage * STAGE + a_base + i * 16 * ROWB);
   };
-  auto read_b = [&](int stage, i32x4 (&fb)[8], int j) __attribute__((always_inline)) {
+  // The next step's B fragment j, in two halves h = 0, 1 (NN: one
+  // transposing read each; NT: one 16-byte read, at h = 0).
+  i32x2 half_lo[8];
+  auto read_b = [&](int stage, i32x4 (&fb)[8], int j, int h) __attribute__((always_inline)) {
     if constexpr (NT) {
-      fb[j] = *(const i32x4 *)(lds + stage * STAGE + bt_base + j * 16 * ROWB);
+      if (h == 0) fb[j] = *(const i32x4 *)(lds + stage * STAGE + bt_base + j * 16 * ROWB);
     } else {
       const char *pb = lds + stage * STAGE + (bn_base ^ (32 * j));
-      const i32x2 lo = __builtin_bit_cast(i32x2, lds_read_tr16(pb));
-      const i32x2 hi = __builtin_bit_cast(i32x2, lds_read_tr16(pb + 4 * NB_ROW));
-      fb[j] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+      if (h == 0) {
+        half_lo[j] = __builtin_bit_cast(i32x2, lds_read_tr16(pb));
+      } else {
+        const i32x2 hi = __builtin_bit_cast(i32x2, lds_read_tr16(pb + 4 * NB_ROW));
+        fb[j] = i32x4{half_lo[j][0], half_lo[j][1], hi[0], hi[1]};
+      }
     }
   };
 
@@ -275,7 +283,10 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) read_a(0, i);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) read_b(0, fb0, j);
+  for (int j = 0; j < 8; ++j) {
+    read_b(0, fb0, j, 0);
+    read_b(0, fb0, j, 1);
+  }
 
   // Step kt: matrix instructions from fa / cb; the next step's fragments into
   // fa (row block by row block, after its last use) and nb -- on the last
@@ -294,8 +305,9 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         acc[i][j] = mma16<AB>(fa[i], cb[j], acc[i][j]);
-        if (j == 1) read_b(nxt, nb, i);
-        if (LOAD && j == 3) issue_one(kt + D, lst, i);
+        if (j == 1) read_b(nxt, nb, i, 0);
+        if (j == 4) read_b(nxt, nb, i, 1);
+        if (LOAD && j == 6) issue_one(kt + D, lst, i);
         __builtin_amdgcn_sched_barrier(0);
       }
       read_a(nxt, i);
