@@ -1,4 +1,4 @@
-// CPU check of load8_u16_words (tiled_matrix_multiplication_amd/csrc/load_words.h),
+// CPU check of load8_u16_words and load8_u16_tail (tiled_matrix_multiplication_amd/csrc/load_words.h),
 // built for the host only and run by tests/test_load_words.py.
 //
 // For both alignments h (p on a 4-byte boundary, or 2 bytes past one) and
@@ -55,6 +55,23 @@ int main() {
       const uint16_t g = (uint16_t)((uint32_t)v[e / 2] >> (16 * (e & 1)));
       if (g != ((const uint16_t *)p)[e]) {
         printf("FAIL interior h=%d element %d\n", h, e);
+        return 1;
+      }
+    }
+    ++checked;
+  }
+  // load8_u16_tail: one 16-byte read ending at the last valid element, or,
+  // for nv == 0, the valid chunk at p; the read ends exactly at the guard
+  // page, so reading one byte more faults.  p = guard - 2 nv takes every
+  // 2-byte alignment modulo 16 as nv runs over 1 .. 8.
+  for (int nv = 0; nv <= 8; ++nv) {
+    const char *p = nv == 0 ? guard - 16 : guard - 2 * nv;
+    const tmm::lw_i32x4 v = tmm::load8_u16_tail(p, nv);
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t g = (uint16_t)((uint32_t)v[e / 2] >> (16 * (e & 1)));
+      const uint16_t want = e < nv ? ((const uint16_t *)p)[e] : 0;
+      if (g != want) {
+        printf("FAIL tail nv=%d element %d: got 0x%04x want 0x%04x\n", nv, e, g, want);
         return 1;
       }
     }

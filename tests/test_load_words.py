@@ -1,8 +1,9 @@
-"""The misaligned 16-bit piece loader of the kernels (load8_u16_words in
-tiled_matrix_multiplication_amd/csrc/load_words.h, compiled for the host
-from the same header) reads nothing past the word holding the last valid
-element, for both alignments and every valid count, and returns the right
-values: tests/load_words_check.hip puts that word against a guard page."""
+"""The misaligned 16-bit piece loaders of the kernels (load8_u16_words and
+load8_u16_tail in tiled_matrix_multiplication_amd/csrc/load_words.h,
+compiled for the host from the same header) read nothing past the word (the
+element) holding the last valid element, for every alignment and valid
+count, and return the right values: tests/load_words_check.hip puts that
+word (element) against a guard page."""
 import os
 import shutil
 import subprocess
@@ -22,4 +23,4 @@ def test_load8_u16_words_stays_before_the_guard_page(tmp_path):
                     os.path.join(ROOT, "tests", "load_words_check.hip"), "-o", exe], check=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, f"rc {r.returncode}: {r.stdout} {r.stderr}"
-    assert r.stdout.startswith("OK 20 windows"), r.stdout
+    assert r.stdout.startswith("OK 29 windows"), r.stdout

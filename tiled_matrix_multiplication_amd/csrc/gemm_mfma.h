@@ -607,13 +607,29 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
     }
   };
 
-  // NN B rows of whole K-step kt into registers.  With N*E a multiple of
-  // 16 a chunk lies wholly inside or wholly outside N; outside ones read
-  // column 0 (nn_src), which only feeds outputs that are never stored.
+  // NN B rows of whole K-step kt into registers: a chunk wholly inside N in
+  // one 16-byte load (any element alignment), the chunk that N cuts through
+  // (16-bit: one 16-byte load ending at its last valid element when rows
+  // hold at least 8 elements, shifted into place when it is stored to LDS;
+  // else by elements) and one wholly past N as zeros (it only feeds outputs
+  // that are never stored).  A per-lane branch around the loads, or work on
+  // the loaded data here, costs the wave its load overlap (4097 x 511 x 1023
+  // bf16: 65 us with a word-load branch for the cut chunk, against 19 us at
+  // N = 512).
+  const bool nn_tail16 = E == 2 && N >= V && N % V != 0;
   auto load_nn_full = [&](int64_t kt) __attribute__((always_inline)) {
     const char *bk = B + kt * BK * p.ldb * E;
 #pragma unroll
-    for (int r = 0; r < RNN; ++r) rb[r] = load16(bk + (nn_src + r * ldb_bytes));
+    for (int r = 0; r < RNN; ++r) {
+      const char *q = bk + (nn_src + r * ldb_bytes);
+      if constexpr (E == 2) {
+        if (N % V == 0) rb[r] = load16(q);  // chunks wholly inside or past N (past: column 0, unused)
+        else if (nn_tail16) rb[r] = load16(tail_load_addr(q, nb_valid));
+        else rb[r] = load_chunk_elems<E>(q, nb_valid);
+      } else {
+        rb[r] = nb_valid == V ? load16(q) : load_chunk_elems<E>(q, nb_valid);
+      }
+    }
   };
 
   // Register path for any K-step: element loads, zero past K (and past N for NN).
@@ -646,8 +662,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
     }
   };
 
-  auto store_nn = [&](int stage) __attribute__((always_inline)) {
+  // `tail`: rb holds load_nn_full's raw loads (the cut chunk still to be
+  // shifted into place), not load_regs' finished chunks.
+  auto store_nn = [&](int stage, bool tail) __attribute__((always_inline)) {
     if constexpr (!NT) {
+      if constexpr (E == 2) {
+        if (tail && nn_tail16) {
+#pragma unroll
+          for (int r = 0; r < RNN; ++r) rb[r] = tail_shift(rb[r], nb_valid);
+        }
+      }
       store_nn_block<E, RNN>(lds + stage * STAGE + A_BYTES, rb, nn_nc * V, nn_kb * RNN * E);
     }
   };
@@ -661,7 +685,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
       for (int i = 0; i < BL; ++i)
         *(i32x4 *)(la + A_BYTES + lds_off((tid >> 3) + (NTH / 8) * i, c)) = rb[i];
     } else {
-      store_nn(stage);
+      store_nn(stage, false);
     }
   };
 
@@ -745,7 +769,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
     if (from_regs)
       store_regs(nxt);
     else
-      store_nn(nxt);
+      store_nn(nxt, true);
     mma_units<AB, FM, FN, 3 * U / 4, U - UL>(acc, fa, fb);
     __builtin_amdgcn_sched_barrier(0);
     stage_barrier();
@@ -761,7 +785,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_kernel(GemmParams p) {
     issue_direct(0, 0);
     if constexpr (!NT) {
       load_nn_full(0);
-      store_nn(0);
+      store_nn(0, true);
     }
   } else {
     load_regs(0);

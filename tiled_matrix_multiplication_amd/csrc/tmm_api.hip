@@ -382,14 +382,19 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
     const int f = forced_tile();
     const bool skinny_ok = vec && trans_b && (ab == TMM_BF16 || ab == TMM_F16);
     const bool generic_forced = forced_generic();
-    // Rows that are not 16-byte aligned (K or N not a multiple of 8 16-bit
-    // elements, e.g. 1000 x 3000 x 777) leave the tiled kernels on word
-    // loads over 128 x 128 tiles.  With an N-contiguous B the any-layout
-    // kernel's 64 x 64 tiles measured faster with operands cold in L2
-    // (bf16: 1000x3000x777 81.1 -> 57.4 us, 4097x511x1023 122.4 -> 102.8);
-    // with a K-contiguous B not clearly (eager, warm: 59 / 59, 77 / 102,
-    // 72 / 63, 234 / 225 us), so NT keeps the tiled kernel.
-    const bool ragged_nn = !vec && !trans_b && f < 0 && (ab == TMM_BF16 || ab == TMM_F16);
+    // 16-byte loads, to registers and direct to LDS, return exact data at
+    // 2-byte-aligned addresses too (measured on gfx950), and the tiled
+    // kernels load a 16-byte chunk whole only when all of it lies inside the
+    // operand (K tails and the chunk an NN B row's end cuts through go by
+    // words, see load_words.h).  So 16-bit and fp32 operands need no more
+    // than their element alignment for the tiled kernels (rows of
+    // 1000 x 3000 x 777 or 4097 x 511 x 1023 bf16).  An NN B whose rows end
+    // inside a 16-byte chunk (N * e % 16 != 0) stays off the ring and
+    // four-wave kernels, whose direct loads move whole chunks.
+    const bool elem16 = ab == TMM_BF16 || ab == TMM_F16 || ab == TMM_F32;
+    const bool loads16 = vec || elem16;
+    const bool nn_cut = !trans_b && (N * e) % 16 != 0;
+    const bool ragged_nn = !loads16 && !trans_b && f < 0 && (ab == TMM_BF16 || ab == TMM_F16);
     if ((generic_forced || ragged_nn) && (ab == TMM_BF16 || ab == TMM_F16)) {
       const int e = elem_bytes(ab);
       const bool va = aligned(A, 16) && (lda * e) % 16 == 0 && (batch == 1 || (sA * e) % 16 == 0);
@@ -416,8 +421,10 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
       const bool vec_c = aligned(C, 4 * ce) && ldc % 4 == 0 && (batch == 1 || sC % 4 == 0);
       err = tmm::launch_gemm_skinny((Fmt)ab, (Fmt)c, bm, bn, vec_c, p, stream);
     } else {
-      const tmm::Tile tile = vec ? pick_tile(M, N, batch, ab) : tmm::kTile128x128;
-      err = dispatch_gemm(ab, c, trans_b != 0, tile, vec, p, stream);
+      tmm::Tile tile = loads16 ? pick_tile(M, N, batch, ab) : tmm::kTile128x128;
+      if (nn_cut && (tile == tmm::kTile256x256 || tile == tmm::kTile256x256r || tile == tmm::kTile256x256q))
+        tile = tmm::kTile256x256s2;
+      err = dispatch_gemm(ab, c, trans_b != 0, tile, loads16, p, stream);
     }
   }
   return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
