@@ -233,10 +233,11 @@ int tmm_version(void);
  * `spec` is a list of key=value items separated by ';' or spaces, NULL or ""
  * for none:
  *   tile=256x256 | 256x128 | 128x128 | 256x256w4 | 256x256s2 | 256x256r |
- *        skinny | generic | shortk | gemvm
+ *        256x256q | 256x128q | 128x128q | skinny | generic | shortk | gemvm
  *                  the GEMM kernel / tile shape wherever it applies
  *                  (256x256s2: two-stage kernel only; 256x256r: the ring
- *                  kernel, K-contiguous B included; skinny, generic, shortk,
+ *                  kernel, K-contiguous B included; ...q: the four-wave
+ *                  kernel with 16x16x32 instructions; skinny, generic, shortk,
  *                  gemvm: the skinny-M, any-layout, short-K and several-row
  *                  GEMV kernels)
  *   skinny=<bm>x<bn>   skinny-M tile, bm and bn in {16, 32, 64}

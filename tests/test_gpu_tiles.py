@@ -96,23 +96,28 @@ QUAD_CASES = [
 ]
 
 
+QUAD_TILES = ["256x256q", "256x128q", "128x128q"]
+
+
+@pytest.mark.parametrize("tile", QUAD_TILES)
 @pytest.mark.parametrize("case", QUAD_CASES, ids=[_id(c) for c in QUAD_CASES])
-def test_quad_kernel(tmm, case, force):
+def test_quad_kernel(tmm, case, tile, force):
     M, N, K, fmt, out, tb, dist, bias, pad = case
-    force("256x256q")
+    force(tile)
     dC, o, T = gemm_case(tmm, M, N, K, fmt, out, tb, dist, bias, seed=300 + 10 * QUAD_CASES.index(case),
                          pad=pad)
-    check(dC, o, T, K, exact=(dist == "int"), what=f"{_id(case)} four-wave")
+    check(dC, o, T, K, exact=(dist == "int"), what=f"{_id(case)} four-wave {tile}")
 
 
+@pytest.mark.parametrize("tile", QUAD_TILES)
 @pytest.mark.parametrize("tb", [False, True], ids=["NN", "NT"])
-def test_quad_kernel_batched(tmm, tb, force):
+def test_quad_kernel_batched(tmm, tb, tile, force):
     """Batch of 3 with padded rows: every slice against the oracle."""
     import numpy as np
     import oracle
     import synthetic as syn
     from gpu_cases import DEV, on_gpu
-    force("256x256q")
+    force(tile)
     Z, M, N, K, pad = 3, 300, 264, 192, 8
     a = syn.to_bits(syn.normal((Z * M, K + pad), 401), "bf16").reshape(Z, M, K + pad)
     bshape = (N, K) if tb else (K, N)

@@ -850,7 +850,7 @@ hipError_t launch_one(const GemmParams &p, hipStream_t stream) {
 template <int AB, int CT, bool NT, int NW>
 hipError_t launch_ring(const GemmParams &p, hipStream_t stream);
 
-template <int AB, int CT, bool NT>
+template <int AB, int CT, bool NT, int BM, int BN>
 hipError_t launch_quad(const GemmParams &p, hipStream_t stream);
 
 template <int AB, int CT, bool NT>
@@ -866,7 +866,7 @@ hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t str
         // 8192x12288x4096 NT 661.6 -> 621.5 us; 8192^3 NN 880 -> 765 us).
         if constexpr (AB == kBF16 || AB == kF16) {
           if (p.K % 64 == 0 && p.K >= 128 && p.beta == 0.f && p.act == 0)
-            return launch_quad<AB, CT, NT>(p, stream);
+            return launch_quad<AB, CT, NT, 256, 256>(p, stream);
         }
         [[fallthrough]];
       case kTile256x256r:
@@ -884,6 +884,17 @@ hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t str
         // registers per lane; fp8 takes four waves (accumulators in AGPRs)
         if constexpr (AB == kF8) return launch_one<AB, CT, NT, 256, 256, 4, true>(p, stream);
         return launch_one<AB, CT, NT, 256, 256, 8, true>(p, stream);
+      case kTile256x128q:
+      case kTile128x128q:
+        // the four-wave kernel on narrower tiles (same conditions as above)
+        if constexpr (AB == kBF16 || AB == kF16) {
+          if (p.K % 64 == 0 && p.K >= 128 && p.beta == 0.f && p.act == 0) {
+            if (tile == kTile256x128q) return launch_quad<AB, CT, NT, 256, 128>(p, stream);
+            return launch_quad<AB, CT, NT, 128, 128>(p, stream);
+          }
+        }
+        if (tile == kTile256x128q) return launch_one<AB, CT, NT, 256, 128, 4, true>(p, stream);
+        return launch_one<AB, CT, NT, 128, 128, 4, true>(p, stream);
       case kTile256x256s2:
         if constexpr (AB == kF8) return launch_one<AB, CT, NT, 256, 256, 4, true>(p, stream);
         return launch_one<AB, CT, NT, 256, 256, 8, true>(p, stream);

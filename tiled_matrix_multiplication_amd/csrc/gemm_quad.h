@@ -72,39 +72,41 @@ __device__ __forceinline__ f32x4 mma16(const i32x4 &a, const i32x4 &b, const f32
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Epilogue of a wave's 128x128 block held as 8x8 16x16 accumulators (lane l:
-// column 16 j + l % 16, rows 16 i + 4 (l / 16) + r): in 32-row bands through
-// the wave's LDS area `st` (rows kQuadPitch bytes apart, 16 bytes of padding
-// so the four 16-lane groups of a write land 16 banks apart) as finished
-// values (scale, bias, one nearest-even rounding), then back 16 bytes per
-// lane along the rows and out with whole-row stores, masked by M and N.
-template <int CT>
-constexpr int quad_pitch() { return 128 * FmtBytes<CT>::value + 16; }
+// Epilogue of a wave's (16 FM) x (16 FN) block held as FM x FN 16x16
+// accumulators (lane l: column 16 j + l % 16, rows 16 i + 4 (l / 16) + r): in
+// 32-row bands through the wave's LDS area `st` (rows quad_pitch bytes
+// apart, 16 bytes of padding so the four 16-lane groups of a write land on
+// distinct banks) as finished values (scale, bias, one nearest-even
+// rounding), then back 16 bytes per lane along the rows and out with
+// whole-row stores, masked by M and N.
+template <int CT, int FN>
+constexpr int quad_pitch() { return 16 * FN * FmtBytes<CT>::value + 16; }
 
-template <int CT>
-__device__ __forceinline__ void store_quad(const f32x4 (&acc)[8][8], char *st, char *C, int64_t ldc,
+template <int CT, int FM, int FN>
+__device__ __forceinline__ void store_quad(const f32x4 (&acc)[FM][FN], char *st, char *C, int64_t ldc,
                                            int64_t M, int64_t N, int64_t row0, int64_t col0,
                                            const float *bias, float scale, int lane) {
   constexpr int CE = FmtBytes<CT>::value;
-  constexpr int P = quad_pitch<CT>();
-  constexpr int CPR = 128 * CE / 16;        // 16-byte pieces per row
+  constexpr int P = quad_pitch<CT, FN>();
+  constexpr int CPR = 16 * FN * CE / 16;    // 16-byte pieces per row
   constexpr int EPC = 16 / CE;              // elements per piece
   constexpr int NRD = 32 * CPR / 64;        // read instructions per band
+  static_assert(FM % 2 == 0 && NRD >= 1 && (32 * CPR) % 64 == 0, "epilogue geometry");
   const int c16 = lane & 15, g = lane >> 4;
   const bool vec = ((uintptr_t)C % 16) == 0 && ((ldc * CE) % 16) == 0;
-  float bv[8];
+  float bv[FN];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < FN; ++j) {
     const int64_t col = col0 + 16 * j + c16;
     bv[j] = (bias && col < N) ? bias[col] : 0.f;
   }
 #pragma unroll
-  for (int band = 0; band < 4; ++band) {
+  for (int band = 0; band < FM / 2; ++band) {
     if (row0 + 32 * band >= M) break;
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * ii + 4 * g + r;
@@ -142,23 +144,30 @@ __device__ __forceinline__ void store_quad(const f32x4 (&acc)[8][8], char *st, c
   }
 }
 
-template <int AB, int CT, bool NT>
+template <int AB, int CT, bool NT, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
-  constexpr int BM = 256, BN = 256, NW = 4;
+  constexpr int NW = 4;
+  constexpr int WTM = BM / 2, WTN = BN / 2;     // each wave's block of C
+  constexpr int FM = WTM / 16, FN = WTN / 16;   // 16x16 accumulators per wave
   constexpr int E = FmtBytes<AB>::value;
   constexpr int CE = FmtBytes<CT>::value;
   constexpr int ROWB = kRingRowBytes;           // 64 bytes of K per tile row per step
   constexpr int BK = ROWB / E;                  // 32
-  constexpr int A_BYTES = BM * ROWB;            // 16 KiB
-  constexpr int B_BYTES = BN * ROWB;            // 16 KiB
+  constexpr int A_BYTES = BM * ROWB;
+  constexpr int B_BYTES = BN * ROWB;
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int S = kRingStages;                // 4
   constexpr int NB_ROW = BN * E;                // NN: bytes of one k-row of the B stage
-  constexpr int LA = A_BYTES / 1024 / NW;       // 4 direct loads per wave per step (A)
-  constexpr int LB = B_BYTES / 1024 / NW;       // 4 (B)
+  constexpr int CPR = NB_ROW / 16, RPI = 64 / CPR;  // NN: chunks per k-row, k-rows per load
+  constexpr int LA = A_BYTES / 1024 / NW;       // direct loads per wave per step (A)
+  constexpr int LB = B_BYTES / 1024 / NW;       // (B)
   constexpr int LPS = LA + LB;
   static_assert(E == 2, "four-wave kernel: 16-bit inputs");
-  static_assert(S == 4 && BK == 32 && NB_ROW == 512, "geometry");
+  static_assert(S == 4 && BK == 32, "geometry");
+  static_assert((BM == 256 || BM == 128) && (BN == 256 || BN == 128) && FM >= FN, "tile shapes");
+  static_assert(LPS <= FM, "one direct load per row block at most");
+  // slots (instruction index within a row block) of the two B half-reads and the load
+  constexpr int QB0 = 1, QB1 = FN >= 8 ? 4 : 3, QD = FN >= 8 ? 6 : 2;
 
   __shared__ __attribute__((aligned(16))) char lds[S * STAGE];
 
@@ -181,8 +190,8 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   const char *B = (const char *)p.B + z * p.strideB * E;
 
   // ---- direct-load sources (byte offsets < 4 GiB, checked by the host).
-  // A and an NT B: instruction i of wave w fills stage rows 64 w + 16 i ..+15;
-  // lane L lands at row L / 4, position L % 4 and loads logical chunk
+  // A and an NT B: instruction i of wave w fills stage rows w BM/4 + 16 i
+  // ..+15; lane L lands at row L / 4, position L % 4 and loads logical chunk
   // (L % 4) ^ swz64(row).  Rows past M (N) read the last valid row.
   uint32_t a_off[LA], b_off[LB];
 #pragma unroll
@@ -199,14 +208,15 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
       b_off[i] = (uint32_t)(r * p.ldb * E + (((lane & 3) ^ swz64(row)) << 4));
     }
   } else {
-    // NN: instruction i of wave w fills k-rows 8 w + 2 i, +1; lane L lands at
-    // k-row L / 32, position L % 32 and loads logical chunk (L % 32) ^
-    // qswz(row).  A chunk wholly past N (the host ensures N * E % 16 == 0)
-    // reads chunk 0 of the tile; it only feeds outputs that are not stored.
+    // NN: instruction i of wave w fills the RPI k-rows from 8 w + RPI i;
+    // lane L lands at k-row L / CPR, position L % CPR and loads logical
+    // chunk (L % CPR) ^ qswz(row).  A chunk wholly past N (the host ensures
+    // N * E % 16 == 0) reads chunk 0 of the tile; it only feeds outputs that
+    // are not stored.
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
-      const int row = wave * (BK / NW) + i * 2 + (lane >> 5);
-      const int c = (lane & 31) ^ qswz(row);
+      const int row = wave * (BK / NW) + i * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ qswz(row);
       const int64_t col = n0 + (int64_t)c * (16 / E);
       const int64_t ccol = col < N ? col : n0;
       b_off[i] = (uint32_t)(((int64_t)row * p.ldb + ccol) * E);
@@ -219,23 +229,25 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   const int l16 = lane & 15, G = lane >> 4;
   // A (and NT B): row block base + lane row l16, chunk G (swizzled)
   const int a_lane = l16 * ROWB + ((G ^ ((l16 >> 2) & 3)) << 4);
-  const int a_base = wm * 128 * ROWB + a_lane;                   // + 1024 i
-  const int bt_base = A_BYTES + wn * 128 * ROWB + a_lane;        // NT: + 1024 j
+  const int a_base = wm * WTM * ROWB + a_lane;                   // + 1024 i
+  const int bt_base = A_BYTES + wn * WTN * ROWB + a_lane;        // NT: + 1024 j
   // NN: lane (G, s = l16) reads k-row 8 G + 4 h + s / 4, columns
-  // 128 wn + 16 j + 4 (s % 4) .. +3; see the header comment for the swizzle.
-  // The block index j only flips the 16 * qswz field: address = base ^ 32 j.
+  // WTN wn + 16 j + 4 (s % 4) .. +3; see the header comment for the swizzle.
+  // The wave's and the block's columns only flip bits of the 16 * qswz
+  // field (or, for the wave of a 256-wide tile, a bit above it): address =
+  // base ^ 2 WTN wn ^ 32 j.
   const int f = 2 * (l16 >> 2) + 8 * (G & 1);
-  const int bn_base = A_BYTES + (8 * G + (l16 >> 2)) * NB_ROW + 256 * wn + 16 * ((l16 & 3) >> 1) +
-                      8 * (l16 & 1) + 16 * f;
+  const int bn_base = (A_BYTES + (8 * G + (l16 >> 2)) * NB_ROW + 16 * ((l16 & 3) >> 1) + 8 * (l16 & 1) +
+                       16 * f) ^ (2 * WTN * wn);
 
-  f32x4 acc[8][8];
+  f32x4 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  i32x4 fa[8];
-  i32x4 fb0[8], fb1[8];
+  i32x4 fa[FM];
+  i32x4 fb0[FN], fb1[FN];
 
   auto issue_one = [&](int64_t kt, int stage, int q) __attribute__((always_inline)) {
     const uint32_t la = lds0 + (uint32_t)(stage * STAGE);
@@ -246,7 +258,7 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
       if constexpr (NT)
         dma16(B + kt * kstep_b + b_off[i], la + A_BYTES + (wave * (BN / NW) + i * 16) * ROWB);
       else
-        dma16(B + kt * kstep_b + b_off[i], la + A_BYTES + (wave * (BK / NW) + i * 2) * NB_ROW);
+        dma16(B + kt * kstep_b + b_off[i], la + A_BYTES + (wave * (BK / NW) + i * RPI) * NB_ROW);
     }
   };
   auto read_a = [&](int stage, int i) __attribute__((always_inline)) {
@@ -254,8 +266,8 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   };
   // The next step's B fragment j, in two halves h = 0, 1 (NN: one
   // transposing read each; NT: one 16-byte read, at h = 0).
-  i32x2 half_lo[8];
-  auto read_b = [&](int stage, i32x4 (&fb)[8], int j, int h) __attribute__((always_inline)) {
+  i32x2 half_lo[FN];
+  auto read_b = [&](int stage, i32x4 (&fb)[FN], int j, int h) __attribute__((always_inline)) {
     if constexpr (NT) {
       if (h == 0) fb[j] = *(const i32x4 *)(lds + stage * STAGE + bt_base + j * 16 * ROWB);
     } else {
@@ -281,33 +293,34 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   else __builtin_amdgcn_s_waitcnt(vm_wait(0));
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) read_a(0, i);
+  for (int i = 0; i < FM; ++i) read_a(0, i);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < FN; ++j) {
     read_b(0, fb0, j, 0);
     read_b(0, fb0, j, 1);
   }
 
   // Step kt: matrix instructions from fa / cb; the next step's fragments into
-  // fa (row block by row block, after its last use) and nb -- on the last
-  // step a harmless read of a stale stage; with LOAD, step kt + 3's direct
-  // loads into the stage step kt - 1 used.  Barrier b(kt) then publishes
-  // step kt + 2 (its loads are waited for first; step kt + 3's stay in
-  // flight).  No vector register depends on a branch: the loop runs the
-  // steps that load, the last three are written out after it.
-  auto step = [&](int64_t kt, const i32x4 (&cb)[8], i32x4 (&nb)[8], auto load_tag)
+  // fa (row block by row block, after its last use) and nb (fragment i in row
+  // block i) -- on the last step a harmless read of a stale stage; with
+  // LOAD, step kt + 3's direct loads (load q in row block q) into the stage
+  // step kt - 1 used.  Barrier b(kt) then publishes step kt + 2 (its loads
+  // are waited for first; step kt + 3's stay in flight).  No vector register
+  // depends on a branch: the loop runs the steps that load, the last three
+  // are written out after it.
+  auto step = [&](int64_t kt, const i32x4 (&cb)[FN], i32x4 (&nb)[FN], auto load_tag)
       __attribute__((always_inline)) {
     constexpr bool LOAD = decltype(load_tag)::value;
     const int nxt = stage_of(kt + 1);
     const int lst = stage_of(kt + D);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < FN; ++j) {
         acc[i][j] = mma16<AB>(fa[i], cb[j], acc[i][j]);
-        if (j == 1) read_b(nxt, nb, i, 0);
-        if (j == 4) read_b(nxt, nb, i, 1);
-        if (LOAD && j == 6) issue_one(kt + D, lst, i);
+        if (i < FN && j == QB0) read_b(nxt, nb, i, 0);
+        if (i < FN && j == QB1) read_b(nxt, nb, i, 1);
+        if (LOAD && i < LPS && j == QD) issue_one(kt + D, lst, i);
         __builtin_amdgcn_sched_barrier(0);
       }
       read_a(nxt, i);
@@ -330,16 +343,16 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   step(kt + 3, fb1, fb0, NoLoad());
 
   // ---- epilogue (the loop's last barrier follows every LDS read of the stages)
-  static_assert(NW * 32 * quad_pitch<CT>() <= S * STAGE, "epilogue staging");
+  static_assert(NW * 32 * quad_pitch<CT, FN>() <= S * STAGE, "epilogue staging");
   char *C = (char *)p.C + z * p.strideC * CE;
-  store_quad<CT>(acc, lds + wave * 32 * quad_pitch<CT>(), C, p.ldc, M, N, m0 + wm * 128, n0 + wn * 128,
-                 p.bias, p.scale, lane);
+  store_quad<CT, FM, FN>(acc, lds + wave * 32 * quad_pitch<CT, FN>(), C, p.ldc, M, N, m0 + wm * WTM,
+                         n0 + wn * WTN, p.bias, p.scale, lane);
 }
 
-template <int AB, int CT, bool NT>
+template <int AB, int CT, bool NT, int BM, int BN>
 hipError_t launch_quad(const GemmParams &p, hipStream_t stream) {
-  const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-  hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
+  hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

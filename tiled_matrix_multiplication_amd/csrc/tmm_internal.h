@@ -28,6 +28,8 @@ enum Tile : int {
   kTile256x256r = 5,   // 256x256 on the ring kernel wherever it applies (also trans_b)
   kTileSkinny = 6,     // the skinny-M kernel (16-bit NT only); chosen in the dispatch
   kTile256x256q = 7,   // 256x256 on the four-wave 128x128-per-wave kernel (16-bit inputs)
+  kTile256x128q = 8,   // 256x128 on the four-wave kernel (128x64 per wave)
+  kTile128x128q = 9,   // 128x128 on the four-wave kernel (64x64 per wave)
   kNumAutoTiles = 3
 };
 
@@ -47,7 +49,7 @@ struct GemmParams {
 };
 
 // Rows/columns of a workgroup tile.
-inline int tile_bm(Tile t) { return t == kTile128x128 ? 128 : 256; }
+inline int tile_bm(Tile t) { return (t == kTile128x128 || t == kTile128x128q) ? 128 : 256; }
 inline int tile_bn(Tile t) {
   return (t == kTile256x256 || t == kTile256x256w4 || t == kTile256x256s2 || t == kTile256x256r ||
           t == kTile256x256q)
