@@ -99,7 +99,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_skinny_kernel(GemmParams p, i
                                                                   int64_t tiles_n, int vec_c) {
   constexpr int kWaves = NW;
   constexpr int FM = BM / 16, FN = BN / 16;
-  constexpr int PITCH = BN + 16;   // floats per LDS row: 16 lanes x 4 rows of a store hit 64 banks
+  // floats per LDS row: a store or tree-step read of one accumulator
+  // register touches 16 consecutive floats of 4 rows 4 apart; with the pitch
+  // 4 more than a multiple of 16 those rows start 16 banks apart, so the
+  // four 16-lane groups cover all 64 banks (the earlier BN + 16 put all four
+  // on the same 16 banks: 50 % of LDS-active cycles were bank conflicts at
+  // M = 256)
+  constexpr int PITCH = BN + 4;
   constexpr int CE = CT == kF32 ? 4 : 2;
   __shared__ __attribute__((aligned(16))) float red[NW / 2][BM][PITCH];
 
