@@ -462,31 +462,36 @@ def read_ceiling(rows=4096, row_bytes=8192, copies=18, waves=(4, 8, 16)):
 
 def mfma_ceiling(flops=2.0 * 4096 ** 3):
     """The matrix cores alone (include/tmm_probes.h, tmmp_mfma_loop): the
-    headline's flops as bf16 matrix instructions on register-resident
-    N(0,1) operands (no loads, no LDS, no stores), 256 workgroups of 8 waves,
-    for both instruction shapes.  Random operands draw more power than zeros,
-    and the chip lowers its clock to stay within its power limit, so this is
-    the rate a GEMM on such data can approach, below the published peak."""
+    headline's flops as matrix instructions on register-resident operands
+    (no loads, no LDS, no stores), 256 workgroups of 8 waves, for each
+    instruction shape: bf16 N(0,1) and zeros, fp8 e4m3 from N(0, 16^2).
+    Random operands draw more power than zeros, and the chip lowers its
+    clock to stay within its power limit, so this is the rate a GEMM on such
+    data can approach, below the published peak."""
     import torch
 
     import tiled_matrix_multiplication_amd.probes as probes
     groups = 256
     iters = int(round(flops / (groups * 8 * (1 << 20))))
+    iters -= iters % 4
     g = torch.Generator(device="cuda:0")
     g.manual_seed(7002)
     ops = torch.randn(1 << 25, device="cuda:0", generator=g).to(torch.bfloat16)
     zeros = torch.zeros_like(ops)
+    ops8 = (torch.randn(1 << 26, device="cuda:0", generator=g) * 16).to(torch.float8_e4m3fn)
     sink = torch.empty(groups * 512, dtype=torch.float32, device="cuda:0")
     out = {}
-    for label, data in (("random", ops), ("zeros", zeros)):
-        for shape, name in ((1, "16x16x32"), (0, "32x32x16")):
-            def run(i, shape=shape, data=data):
-                probes.mfma_loop(data, shape, groups, iters, sink)
-            ms, _ = time_steps(run, 50, 5)
-            tf = groups * 8 * iters * (1 << 20) / (ms * 1e-3) / 1e12
-            out[f"{label}_{name}"] = {"us_per_launch": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
-                                      "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
-    del ops, zeros
+    cases = (("random", ops, 1, "16x16x32", "bf16"), ("random", ops, 0, "32x32x16", "bf16"),
+             ("zeros", zeros, 1, "16x16x32", "bf16"), ("zeros", zeros, 0, "32x32x16", "bf16"),
+             ("random_fp8", ops8, 3, "16x16x128", "e4m3"), ("random_fp8", ops8, 2, "32x32x64", "e4m3"))
+    for label, data, shape, name, fmt in cases:
+        def run(i, shape=shape, data=data):
+            probes.mfma_loop(data, shape, groups, iters, sink)
+        ms, _ = time_steps(run, 50, 5)
+        tf = groups * 8 * iters * (1 << 20) / (ms * 1e-3) / 1e12
+        out[f"{label}_{name}"] = {"us_per_launch": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+                                  "frac_of_peak": round(tf / PEAK_TFLOPS[fmt], 4)}
+    del ops, zeros, ops8
     return out
 
 
@@ -926,7 +931,7 @@ def main(argv=None):
         line["gpu_state"] = gpu_state_under_load(launcher(name, r["sets"], None, 1.0, 1.0))
     if name == "square_bf16" and not args.no_ceilings:
         c = mfma_ceiling()
-        best = max(v["TFLOP/s"] for k, v in c.items() if k.startswith("random"))
+        best = max(v["TFLOP/s"] for k, v in c.items() if k.startswith("random_") and "fp8" not in k)
         line["mfma_ceiling"] = dict(c, note="bf16 matrix instructions alone on register-resident operands, the "
                                             "headline's flops; the chip's clock falls under random data",
                                     headline_frac_of_random_ceiling=round(value / best, 4))

@@ -26,8 +26,10 @@
  *     the accumulators of a 128x64 block (per wave), cycling through 4
  *     K-steps of fragments, so the operands change every instruction as in
  *     a GEMM.  shape 0: v_mfma_f32_32x32x16_bf16 (32 per round), shape 1:
- *     v_mfma_f32_16x16x32_bf16 (64 per round); 1 Mi flop per round either
- *     way.  `operands` holds operand_bytes >= max(16 MiB, groups x 192 KiB)
+ *     v_mfma_f32_16x16x32_bf16 (64 per round), shape 2: the fp8 (e4m3)
+ *     32x32x64 (8 per round), shape 3: the fp8 16x16x128 (16 per round);
+ *     1 Mi flop per round in every case (shapes 2, 3: iters a multiple of
+ *     4; the fp8 operands are the same bytes read as e4m3).  `operands` holds operand_bytes >= max(16 MiB, groups x 192 KiB)
  *     of bf16 data (each thread reads its own 384 bytes; the caller's
  *     values: random data draws more power than zeros); `sink` (device)
  *     receives one float per thread, groups * 512 floats.
