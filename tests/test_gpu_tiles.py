@@ -132,3 +132,23 @@ def test_quad_kernel_batched(tmm, tb, tile, force):
         o, T = oracle.gemm("bf16", np.ascontiguousarray(a[z][:, :K]), np.ascontiguousarray(b[z][:, :bshape[1]]),
                            trans_b=tb, bias=bvec, want_abs=True)
         check(C[z], o, T, K, what=f"four-wave batch {z}")
+
+
+# The fp8 four-wave kernel (gemm_quad8.h): K a multiple of 128 and at least
+# 256; chunks of 16 fp8 whole (N % 16 == 0 for an N-contiguous B).
+QUAD8_CASES = [
+    (512, 512, 512, "e4m3", "bf16", False, "normal", False, 0),
+    (384, 640, 512, "e4m3", "f32", True, "normal", True, 0),
+    (300, 528, 256, "e4m3", "bf16", False, "int", True, 16),
+    (256, 256, 1024, "e4m3", "f32", False, "normal", False, 0),
+    (520, 272, 384, "e4m3", "bf16", True, "int", False, 0),
+]
+
+
+@pytest.mark.parametrize("case", QUAD8_CASES, ids=[_id(c) for c in QUAD8_CASES])
+def test_quad8_kernel(tmm, case, force):
+    M, N, K, fmt, out, tb, dist, bias, pad = case
+    force("256x256q")
+    dC, o, T, ops = gemm_case(tmm, M, N, K, fmt, out, tb, dist, bias, seed=500 + 10 * QUAD8_CASES.index(case),
+                              pad=pad, want_ops=True)
+    check(dC, o, T, K, exact=(dist == "int"), what=f"{_id(case)} fp8 four-wave", f8=True, f8_ops=ops)

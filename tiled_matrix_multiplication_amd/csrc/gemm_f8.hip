@@ -2,6 +2,7 @@
 // unit per input type so the kernels build in parallel).
 #include "gemm_mfma.h"
 #include "gemm_ring.h"
+#include "gemm_quad8.h"
 
 namespace tmm {
 
