@@ -78,7 +78,8 @@ def test_layouts(tmm, ta, tb, fmt, out, M, force):
              what=f"{'T' if ta else 'N'}{'T' if tb else 'N'} {fmt}->{out} M {M}")
 
 
-TILES = ["256x256", "256x256r", "256x256s2", "256x256w4", "256x128", "128x128", "skinny", "generic"]
+TILES = ["256x256", "256x256r", "256x256s2", "256x256w4", "256x128", "128x128", "skinny", "generic",
+         "256x256q", "256x128q", "128x128q"]
 
 
 @pytest.mark.parametrize("tile", TILES)
@@ -101,6 +102,18 @@ def test_integer_inputs_exact(tmm, force):
                  dist="int", what=f"int {ta}{tb}")
         run_case(tmm, 300, 270, 64, "f16", "f16", ta, tb, 2.0, -1.0, True, True, seed=1210,
                  dist="int", what=f"int f16 {ta}{tb}")
+
+
+@pytest.mark.parametrize("tile", ["256x256q", "256x128q", "128x128q"])
+def test_four_wave_full_form_integer_exact(tmm, tile, force):
+    """The four-wave kernel's full-form epilogue, bit for bit on small
+    integers (K a multiple of 64, at least 128), both B layouts."""
+    force(tile)
+    for tb in (False, True):
+        run_case(tmm, 300, 272, 128, "bf16", "f32", False, tb, 2.0, -1.0, True, True, seed=1250, dist="int",
+                 what=f"int {tile} {'NT' if tb else 'NN'}")
+        run_case(tmm, 264, 520, 192, "f16", "f16", False, tb, -1.0, 0.5, True, False, seed=1260, dist="int",
+                 what=f"int f16 {tile} {'NT' if tb else 'NN'}")
 
 
 def test_fp8_and_fp32(tmm, force):

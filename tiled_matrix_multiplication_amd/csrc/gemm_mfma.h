@@ -863,13 +863,12 @@ hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t str
       case kTile256x256:
       case kTile256x256q:
         // Four-wave kernel (gemm_quad.h): 16-bit inputs, an even number (at
-        // least 4) of 32-element K-steps, the plain form.  Chosen for every
+        // least 4) of 32-element K-steps, the plain or full form.  Chosen for every
         // such 256x256 tile: it measured faster than the ring and two-stage
         // kernels at every shape timed (4096^3 NN fp32 out 118.1 -> 102.3 us;
         // 8192x12288x4096 NT 661.6 -> 621.5 us; 8192^3 NN 880 -> 765 us).
         if constexpr (AB == kBF16 || AB == kF16) {
-          if (p.K % 64 == 0 && p.K >= 128 && p.beta == 0.f && p.act == 0)
-            return launch_quad<AB, CT, NT, 256, 256>(p, stream);
+          if (p.K % 64 == 0 && p.K >= 128) return launch_quad<AB, CT, NT, 256, 256>(p, stream);
         }
         // fp8: the four-wave kernel of gemm_quad8.h (an even number, at least
         // 4, of 64-element K-steps; the plain form): 8192^3 NN bf16 out
@@ -897,7 +896,7 @@ hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t str
       case kTile128x128q:
         // the four-wave kernel on narrower tiles (same conditions as above)
         if constexpr (AB == kBF16 || AB == kF16) {
-          if (p.K % 64 == 0 && p.K >= 128 && p.beta == 0.f && p.act == 0) {
+          if (p.K % 64 == 0 && p.K >= 128) {
             if (tile == kTile256x128q) return launch_quad<AB, CT, NT, 256, 128>(p, stream);
             return launch_quad<AB, CT, NT, 128, 128>(p, stream);
           }

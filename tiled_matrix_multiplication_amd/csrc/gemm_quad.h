@@ -2,7 +2,8 @@
 // wave owning a 128x128 block of C: the kernel for 16-bit inputs whose rows
 // are 16-byte aligned and whose K is a multiple of 64, at least 128.
 //
-//   C[z] = scale * A[z] . op(B[z]) (+ bias),  row-major, z < batch
+//   C[z] = act(scale * A[z] . op(B[z]) (+ bias) (+ beta * old C[z])),
+//   row-major, z < batch, act = identity or ReLU
 //
 // It keeps the four-stage LDS ring of gemm_ring.h (same stage size, same
 // direct 16-byte global->LDS loads issued three K-steps ahead, same
@@ -76,13 +77,13 @@ __device__ __forceinline__ f32x4 mma16(const i32x4 &a, const i32x4 &b, const f32
 // accumulators (lane l: column 16 j + l % 16, rows 16 i + 4 (l / 16) + r): in
 // 32-row bands through the wave's LDS area `st` (rows quad_pitch bytes
 // apart, 16 bytes of padding so the four 16-lane groups of a write land on
-// distinct banks) as finished values (scale, bias, one nearest-even
-// rounding), then back 16 bytes per lane along the rows and out with
+// distinct banks) as finished values (scale, bias, ReLU when RELU, one
+// nearest-even rounding), then back 16 bytes per lane along the rows and out with
 // whole-row stores, masked by M and N.
 template <int CT, int FN>
 constexpr int quad_pitch() { return 16 * FN * FmtBytes<CT>::value + 16; }
 
-template <int CT, int FM, int FN>
+template <int CT, int FM, int FN, bool RELU>
 __device__ __forceinline__ void store_quad(const f32x4 (&acc)[FM][FN], char *st, char *C, int64_t ldc,
                                            int64_t M, int64_t N, int64_t row0, int64_t col0,
                                            const float *bias, float scale, int lane) {
@@ -110,7 +111,9 @@ __device__ __forceinline__ void store_quad(const f32x4 (&acc)[FM][FN], char *st,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * ii + 4 * g + r;
-          const uint32_t b = out_bits<CT>(acc[2 * band + ii][j][r] * scale + bv[j]);
+          float v = acc[2 * band + ii][j][r] * scale + bv[j];
+          if constexpr (RELU) v = v > 0.f ? v : 0.f;
+          const uint32_t b = out_bits<CT>(v);
           char *d = st + row * P + (16 * j + c16) * CE;
           if constexpr (CE == 4) *(uint32_t *)d = b;
           else *(uint16_t *)d = (uint16_t)b;
@@ -144,7 +147,102 @@ __device__ __forceinline__ void store_quad(const f32x4 (&acc)[FM][FN], char *st,
   }
 }
 
-template <int AB, int CT, bool NT, int BM, int BN>
+// Full-form epilogue of the same block, C = act(alpha acc + bias + beta C_old):
+// fp32 values (alpha acc + bias) staged per 32-row band as above, read back
+// 4 columns per lane; the old C of those 4 columns is read when beta != 0 (a
+// vector load when C and its pitch allow), then ReLU when act == 1 and one
+// nearest-even rounding.
+template <int CT, int FN>
+constexpr int quad_ex_pitch() { return 16 * FN * 4 + 16; }
+
+template <int CT, int FM, int FN>
+__device__ __forceinline__ void store_quad_ex(const f32x4 (&acc)[FM][FN], char *st, char *C, int64_t ldc,
+                                              int64_t M, int64_t N, int64_t row0, int64_t col0,
+                                              const float *bias, float alpha, float beta, int act, int lane) {
+  constexpr int CE = FmtBytes<CT>::value;
+  constexpr int P = quad_ex_pitch<CT, FN>();
+  constexpr int QPR = 4 * FN;               // 4-column quads per row
+  constexpr int NRD = 32 * QPR / 64;        // read instructions per band
+  static_assert(FM % 2 == 0 && NRD >= 1, "epilogue geometry");
+  const int c16 = lane & 15, g = lane >> 4;
+  const bool vec = ((uintptr_t)C % (4 * CE)) == 0 && (ldc % 4) == 0;
+  float bv[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t col = col0 + 16 * j + c16;
+    bv[j] = (bias && col < N) ? bias[col] : 0.f;
+  }
+#pragma unroll
+  for (int band = 0; band < FM / 2; ++band) {
+    if (row0 + 32 * band >= M) break;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *(float *)(st + (16 * ii + 4 * g + r) * P + (16 * j + c16) * 4) = acc[2 * band + ii][j][r] * alpha + bv[j];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    // two quads in flight at a time: the old C values of a fully unrolled
+    // band would need more registers than the accumulators leave free
+#pragma unroll 2
+    for (int t = 0; t < NRD; ++t) {
+      const int qd = t * 64 + lane;
+      const int lr = qd / QPR, qc = qd % QPR;
+      f32x4 v = *(const f32x4 *)(st + lr * P + qc * 16);
+      const int64_t grow = row0 + 32 * band + lr;
+      const int64_t gcol = col0 + (int64_t)qc * 4;
+      if (grow >= M || gcol >= N) continue;
+      char *dst = C + (grow * ldc + gcol) * CE;
+      const bool full = vec && gcol + 4 <= N;
+      if (beta != 0.f) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        if (full) {
+          if constexpr (CE == 4) {
+            c = *(const f32x4 *)dst;
+          } else {
+            const uint64_t w = *(const uint64_t *)dst;
+            c = f32x4{in_value<CT>((uint16_t)w), in_value<CT>((uint16_t)(w >> 16)),
+                      in_value<CT>((uint16_t)(w >> 32)), in_value<CT>((uint16_t)(w >> 48))};
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (gcol + e < N) {
+              if constexpr (CE == 4) c[e] = ((const float *)dst)[e];
+              else c[e] = in_value<CT>(((const uint16_t *)dst)[e]);
+            }
+          }
+        }
+        v += beta * c;
+      }
+      if (act == 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = v[e] > 0.f ? v[e] : 0.f;
+      }
+      if (full) {
+        if constexpr (CE == 4) {
+          *(f32x4 *)dst = v;
+        } else {
+          const uint64_t w = (uint64_t)out_bits<CT>(v[0]) | ((uint64_t)out_bits<CT>(v[1]) << 16) |
+                             ((uint64_t)out_bits<CT>(v[2]) << 32) | ((uint64_t)out_bits<CT>(v[3]) << 48);
+          *(uint64_t *)dst = w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (gcol + e < N) store_out<CT>(dst, e, v[e]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next band's writes
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// EPI: 0 the plain epilogue, 1 the plain one with ReLU, 2 the full form
+// (old C read back)
+template <int AB, int CT, bool NT, int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   constexpr int NW = 4;
   constexpr int WTM = BM / 2, WTN = BN / 2;     // each wave's block of C
@@ -343,16 +441,29 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   step(kt + 3, fb1, fb0, NoLoad());
 
   // ---- epilogue (the loop's last barrier follows every LDS read of the stages)
-  static_assert(NW * 32 * quad_pitch<CT, FN>() <= S * STAGE, "epilogue staging");
   char *C = (char *)p.C + z * p.strideC * CE;
-  store_quad<CT, FM, FN>(acc, lds + wave * 32 * quad_pitch<CT, FN>(), C, p.ldc, M, N, m0 + wm * WTM,
-                         n0 + wn * WTN, p.bias, p.scale, lane);
+  if constexpr (EPI == 2) {
+    static_assert(NW * 32 * quad_ex_pitch<CT, FN>() <= S * STAGE, "epilogue staging");
+    store_quad_ex<CT, FM, FN>(acc, lds + wave * 32 * quad_ex_pitch<CT, FN>(), C, p.ldc, M, N, m0 + wm * WTM,
+                              n0 + wn * WTN, p.bias, p.scale, p.beta, p.act, lane);
+  } else {
+    static_assert(NW * 32 * quad_pitch<CT, FN>() <= S * STAGE, "epilogue staging");
+    store_quad<CT, FM, FN, EPI == 1>(acc, lds + wave * 32 * quad_pitch<CT, FN>(), C, p.ldc, M, N, m0 + wm * WTM,
+                           n0 + wn * WTN, p.bias, p.scale, lane);
+  }
 }
 
 template <int AB, int CT, bool NT, int BM, int BN>
 hipError_t launch_quad(const GemmParams &p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
-  hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  // each epilogue in its own instantiation, so the plain kernel's code is
+  // what it was without the others; only beta != 0 reads the old C
+  if (p.beta != 0.f)
+    hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN, 2>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  else if (p.act == 1)
+    hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN, 1>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN, 0>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
