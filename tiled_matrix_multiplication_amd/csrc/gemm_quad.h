@@ -48,6 +48,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "gemm_mfma.h"
 #include "gemm_ring.h"
@@ -147,13 +148,27 @@ __device__ __forceinline__ void store_quad(const f32x4 (&acc)[FM][FN], char *st,
   }
 }
 
-// Full-form epilogue of the same block, C = act(alpha acc + bias + beta C_old):
-// fp32 values (alpha acc + bias) staged per 32-row band as above, read back
-// 4 columns per lane; the old C of those 4 columns is read when beta != 0 (a
-// vector load when C and its pitch allow), then ReLU when act == 1 and one
-// nearest-even rounding.
+// Full-form epilogue of the same block, C = act(alpha acc + bias + beta C_old),
+// beta != 0: per 32-row band, the old C of the 4-column quads this lane will
+// write is loaded first (as stored: 16-bit words or fp32, a vector load when
+// C and its pitch allow), so that those loads are in flight while the fp32
+// values (alpha acc + bias) are staged through LDS as above; then each quad
+// is read back, beta C_old added, ReLU when act == 1, one nearest-even
+// rounding, and stored.
 template <int CT, int FN>
 constexpr int quad_ex_pitch() { return 16 * FN * 4 + 16; }
+
+template <int CT>
+struct OldQuad { typedef uint64_t type; };  // four 16-bit words
+template <>
+struct OldQuad<kF32> { typedef f32x4 type; };
+
+// Calls f(integral_constant<int, 0>), f(..1), ... in order while it
+// returns true.
+template <typename F, int... I>
+__device__ __forceinline__ void each_band(F &f, std::integer_sequence<int, I...>) {
+  (void)(... && f(std::integral_constant<int, I>()));
+}
 
 template <int CT, int FM, int FN>
 __device__ __forceinline__ void store_quad_ex(const f32x4 (&acc)[FM][FN], char *st, char *C, int64_t ldc,
@@ -162,8 +177,9 @@ __device__ __forceinline__ void store_quad_ex(const f32x4 (&acc)[FM][FN], char *
   constexpr int CE = FmtBytes<CT>::value;
   constexpr int P = quad_ex_pitch<CT, FN>();
   constexpr int QPR = 4 * FN;               // 4-column quads per row
-  constexpr int NRD = 32 * QPR / 64;        // read instructions per band
+  constexpr int NRD = 32 * QPR / 64;        // quads per lane per band
   static_assert(FM % 2 == 0 && NRD >= 1, "epilogue geometry");
+  typedef typename OldQuad<CT>::type Old;
   const int c16 = lane & 15, g = lane >> 4;
   const bool vec = ((uintptr_t)C % (4 * CE)) == 0 && (ldc % 4) == 0;
   float bv[FN];
@@ -172,9 +188,34 @@ __device__ __forceinline__ void store_quad_ex(const f32x4 (&acc)[FM][FN], char *
     const int64_t col = col0 + 16 * j + c16;
     bv[j] = (bias && col < N) ? bias[col] : 0.f;
   }
+  // one band per call, its index a constant: the accumulators are only ever
+  // indexed by constants, so they stay in registers however large the body
+  auto do_band = [&](auto band_c) -> bool {
+    constexpr int band = decltype(band_c)::value;
+    if (row0 + 32 * band >= M) return false;
+    Old old[NRD];
 #pragma unroll
-  for (int band = 0; band < FM / 2; ++band) {
-    if (row0 + 32 * band >= M) break;
+    for (int t = 0; t < NRD; ++t) {
+      const int qd = t * 64 + lane;
+      const int64_t grow = row0 + 32 * band + qd / QPR;
+      const int64_t gcol = col0 + (int64_t)(qd % QPR) * 4;
+      const char *src = C + (grow * ldc + gcol) * CE;
+      if (grow < M && gcol + 4 <= N && vec) {
+        old[t] = *(const Old *)src;
+      } else {
+        Old w = {};
+        if (grow < M) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (gcol + e < N) {
+              if constexpr (CE == 4) w[e] = ((const float *)src)[e];
+              else w |= (uint64_t)((const uint16_t *)src)[e] << (16 * e);
+            }
+          }
+        }
+        old[t] = w;
+      }
+    }
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -184,9 +225,7 @@ __device__ __forceinline__ void store_quad_ex(const f32x4 (&acc)[FM][FN], char *
           *(float *)(st + (16 * ii + 4 * g + r) * P + (16 * j + c16) * 4) = acc[2 * band + ii][j][r] * alpha + bv[j];
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
-    // two quads in flight at a time: the old C values of a fully unrolled
-    // band would need more registers than the accumulators leave free
-#pragma unroll 2
+#pragma unroll
     for (int t = 0; t < NRD; ++t) {
       const int qd = t * 64 + lane;
       const int lr = qd / QPR, qc = qd % QPR;
@@ -195,33 +234,20 @@ __device__ __forceinline__ void store_quad_ex(const f32x4 (&acc)[FM][FN], char *
       const int64_t gcol = col0 + (int64_t)qc * 4;
       if (grow >= M || gcol >= N) continue;
       char *dst = C + (grow * ldc + gcol) * CE;
-      const bool full = vec && gcol + 4 <= N;
-      if (beta != 0.f) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
-        if (full) {
-          if constexpr (CE == 4) {
-            c = *(const f32x4 *)dst;
-          } else {
-            const uint64_t w = *(const uint64_t *)dst;
-            c = f32x4{in_value<CT>((uint16_t)w), in_value<CT>((uint16_t)(w >> 16)),
-                      in_value<CT>((uint16_t)(w >> 32)), in_value<CT>((uint16_t)(w >> 48))};
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (gcol + e < N) {
-              if constexpr (CE == 4) c[e] = ((const float *)dst)[e];
-              else c[e] = in_value<CT>(((const uint16_t *)dst)[e]);
-            }
-          }
-        }
-        v += beta * c;
+      f32x4 c;
+      if constexpr (CE == 4) {
+        c = old[t];
+      } else {
+        const uint64_t w = old[t];
+        c = f32x4{in_value<CT>((uint16_t)w), in_value<CT>((uint16_t)(w >> 16)),
+                  in_value<CT>((uint16_t)(w >> 32)), in_value<CT>((uint16_t)(w >> 48))};
       }
+      v += beta * c;
       if (act == 1) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = v[e] > 0.f ? v[e] : 0.f;
       }
-      if (full) {
+      if (vec && gcol + 4 <= N) {
         if constexpr (CE == 4) {
           *(f32x4 *)dst = v;
         } else {
@@ -237,7 +263,9 @@ __device__ __forceinline__ void store_quad_ex(const f32x4 (&acc)[FM][FN], char *
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next band's writes
     __builtin_amdgcn_wave_barrier();
-  }
+    return true;
+  };
+  each_band(do_band, std::make_integer_sequence<int, FM / 2>());
 }
 
 // EPI: 0 the plain epilogue, 1 the plain one with ReLU, 2 the full form
