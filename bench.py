@@ -557,12 +557,12 @@ CSRC = os.path.join(ROOT, "tiled_matrix_multiplication_amd", "csrc")
 # Sources that define each workload's dominant kernel (the host dispatch and
 # the shared parameter header are not part of it).
 KERNEL_SOURCES = {
-    "gemm": ["gemm_mfma.h", "gemm_ring.h", "gemm_quad.h", "load_words.h", "gemm_f32.hip", "gemm_bf16.hip",
-             "gemm_f16.hip", "gemm_f8.hip", "gemm_ring_ta.hip", "gemm_short_k.hip"],
+    "gemm": ["gemm_mfma.h", "gemm_ring.h", "gemm_quad.h", "gemm_quad8.h", "load_words.h", "gemm_f32.hip",
+             "gemm_bf16.hip", "gemm_f16.hip", "gemm_f8.hip", "gemm_ring_ta.hip", "gemm_short_k.hip"],
     "gemv": ["gemv.hip"],
     "skinny": ["gemm_skinny.hip"],
     "attention": ["attention.hip"],
-    "conv": ["conv_implicit.hip"],
+    "conv": ["conv_implicit.hip", "conv_quad.h", "gemm_quad.h", "gemm_ring.h", "gemm_mfma.h"],
 }
 
 
@@ -626,7 +626,7 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
     elif name.startswith("skinny"):
         kernel_substr = "gemm_skinny"
     elif name in CONV:
-        kernel_substr = "conv_implicit"
+        kernel_substr = "conv_"   # conv_implicit_kernel or conv_quad_kernel
     f_k, nf = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", kernel_substr)
     w_k, nw = _counter_per_dispatch(write_csv, "WRITE_SIZE", kernel_substr)
     f_c, _ = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", copy_substr)

@@ -238,9 +238,11 @@ def test_override_accepts_the_documented_keys_and_rejects_others(tmm):
     the setting as it was and returns TMM_ERR_ARG."""
     try:
         for spec in ["", "tile=128x128", "tile=skinny;skinny=32x64", "tile=gemvm", "gemv=2x16",
-                     "tile=shortk skinny=16x16 gemv=1x4", "tile=generic", "tile=256x256r"]:
+                     "tile=shortk skinny=16x16 gemv=1x4", "tile=generic", "tile=256x256r",
+                     "conv=quad", "conv=direct;tile=256x256q"]:
             assert tmm.lib.tmm_set_override(spec.encode()) == 0, spec
-        for spec in ["tile=99x99", "skinny=8x16", "gemv=3x4", "gemv=2,16", "foo=1", "tile", "tile=128x128;x"]:
+        for spec in ["tile=99x99", "skinny=8x16", "gemv=3x4", "gemv=2,16", "foo=1", "tile", "tile=128x128;x",
+                     "conv=fast"]:
             assert tmm.lib.tmm_set_override(spec.encode()) == -9, spec
         assert tmm.lib.tmm_set_override(None) == 0
     finally:
@@ -272,7 +274,8 @@ def test_probe_arguments_checked_on_host():
     assert lib.tmmp_stream_read(ctypes.c_void_p(0x100004), 4, 8192, 16, sink, None) == -7
     assert lib.tmmp_stream_read(FAKE, 0, 8192, 16, sink, None) == 0       # nothing to read
     assert lib.tmmp_mfma_loop(FAKE, 1 << 20, 1, 256, 64, sink, None) == -1  # operands under 16 MiB
-    assert lib.tmmp_mfma_loop(FAKE, 1 << 24, 2, 256, 64, sink, None) == -9  # shape
+    assert lib.tmmp_mfma_loop(FAKE, 1 << 24, 4, 256, 64, sink, None) == -9  # shape
+    assert lib.tmmp_mfma_loop(FAKE, 1 << 24, 2, 4, 65, sink, None) == -1    # fp8 shapes: iters % 4
     assert lib.tmmp_mfma_loop(None, 1 << 24, 1, 4, 64, sink, None) == -3
     assert lib.tmmp_mfma_loop(FAKE, 1 << 24, 1, 256, 64, sink, None) == -1  # 256 groups need 48 MiB
     assert lib.tmmp_mfma_loop(FAKE, 1 << 24, 1, 0, 64, sink, None) == 0

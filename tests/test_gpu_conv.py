@@ -91,6 +91,43 @@ def test_without_scale_and_bias(tmm):
     run(tmm, 2, 8, 8, 16, 32, 3, 3, 1, "bf16", "f32", False, 1, seed=2300, scale=False, bias=False)
 
 
+# Channel counts that are multiples of 32, for the LDS-staged kernel (256
+# pixels x 128 filters per workgroup, one tap per 32-channel K-step):
+# pixels and filters that end mid-tile, two filter tiles, R != S with wide
+# padding, an odd step count (padded with a zero step), the fewest steps it
+# takes (1 x 1, C = 96: three, padded to four), no padding.
+QUAD_CASES = [
+    (8, 64, 64, 32, 64, 3, 3, 1, "bf16", "f32", True, 2),
+    (2, 17, 13, 32, 100, 3, 3, 1, "bf16", "bf16", False, 1),
+    (3, 10, 12, 64, 130, 3, 3, 1, "f16", "f32", True, 2),
+    (1, 9, 9, 32, 64, 5, 3, 2, "bf16", "f32", True, 1),
+    (2, 14, 14, 96, 128, 1, 1, 0, "f16", "f16", False, 2),
+    (1, 6, 6, 32, 16, 3, 3, 0, "bf16", "bf16", True, 2),
+    (2, 11, 7, 160, 200, 3, 3, 1, "f16", "f16", True, 1),
+]
+
+
+@pytest.mark.parametrize("case", QUAD_CASES, ids=[_id(c) for c in QUAD_CASES])
+def test_lds_staged_kernel(tmm, force, case):
+    N, H, W, C, K, R, S, pad, fmt, out, relu, pool = case
+    force(conv="quad")
+    run(tmm, N, H, W, C, K, R, S, pad, fmt, out, relu, pool, seed=2500 + 10 * QUAD_CASES.index(case))
+
+
+def test_lds_staged_kernel_integer_exact(tmm, force):
+    """Bit-exact on small integers through the LDS-staged kernel, pooled and
+    not, with the zero taps of the halo and a padded step."""
+    force(conv="quad")
+    run(tmm, 2, 12, 10, 32, 72, 3, 3, 1, "bf16", "f32", True, 2, seed=2600, dist="int")
+    run(tmm, 2, 12, 10, 32, 40, 5, 3, 2, "f16", "f16", False, 1, seed=2610, dist="int")
+
+
+def test_lds_staged_kernel_is_chosen_for_full_grids(tmm):
+    """16 x 64 x 64 pixels, C = 32: 256 workgroups of 256 x 128, enough for
+    the automatic choice to be the LDS-staged kernel (no override)."""
+    run(tmm, 16, 64, 64, 32, 128, 3, 3, 1, "bf16", "bf16", True, 2, seed=2700)
+
+
 @pytest.mark.parametrize("case", [
     (17, 31, 31, 8, 520, 3, 3, 1, "bf16", "bf16", True, 1),   # pixels end mid-tile, K not a multiple of 64
     (16, 32, 32, 16, 512, 3, 3, 1, "f16", "f32", True, 2),    # pooled windows

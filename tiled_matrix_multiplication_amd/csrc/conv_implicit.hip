@@ -27,6 +27,7 @@
 //     nearest-even rounding, store (NHWC output).
 #include <stdint.h>
 
+#include "conv_quad.h"
 #include "tmm_internal.h"
 
 namespace tmm {
@@ -242,9 +243,18 @@ __global__ __launch_bounds__(256, 2) void conv_implicit_kernel(ConvParams p) {
 // gives two workgroups per CU; 32 otherwise.  64 x 64^2 x 64 -> 128, 3x3,
 // pool: 204.8 -> 147.8 us; the 8 x 64^2 x 32 -> 64 problem (128 tiles of 256
 // pixels) measured 9.8 us with 32 and 12.8 us with 64.
+//
+// The LDS-staged kernel of conv_quad.h takes channel counts C % 32 == 0
+// (one tap per K-step) with R S C >= 96 (at least 4 steps) when its
+// 256 x 128 tiles fill every CU at least once.
 template <int AB, int CT>
 hipError_t launch_typed(const ConvParams &p, hipStream_t stream) {
   const int64_t P = p.H + 2 * p.pad - p.R + 1, Q = p.W + 2 * p.pad - p.S + 1;
+  const int ov = conv_override();
+  const bool quad_ok = p.C % 32 == 0 && (int64_t)p.R * p.S * p.C >= 96;
+  const int64_t quad_tiles = ((p.N * P * Q + 255) / 256) * ((p.K + 127) / 128);
+  if (quad_ok && (ov == 1 || (ov == 0 && quad_tiles >= (int64_t)device_cu_count())))
+    return gemm_detail::launch_conv_quad<AB, CT>(p, stream);
   const int64_t tn = (p.K + kBN - 1) / kBN;
   const int64_t t256 = ((p.N * P * Q + 255) / 256) * tn;
   if (t256 >= 2 * (int64_t)device_cu_count()) {

@@ -47,6 +47,7 @@ int gemv_override() {
   const uint64_t ov = override_word();
   return (int)((ov >> 24) & 0xff) * 100 + (int)((ov >> 32) & 0xff);
 }
+int conv_override() { return (int)((override_word() >> 40) & 3); }
 }  // namespace tmm
 
 namespace {
@@ -178,6 +179,12 @@ bool parse_override(const char *spec, uint64_t *out) {
           (w != 4 && w != 8 && w != 16))
         return false;
       v = (v & ~(0xffffull << 24)) | ((uint64_t)r << 24) | ((uint64_t)w << 32);
+    } else if (!strcmp(key, "conv")) {
+      uint64_t c = 0;
+      if (!strcmp(val, "quad")) c = 1;
+      else if (!strcmp(val, "direct")) c = 2;
+      else return false;
+      v = (v & ~(3ull << 40)) | (c << 40);
     } else {
       return false;
     }

@@ -13,6 +13,10 @@ int device_cu_count();
 // GEMV launch shape pinned by the library's override (R * 100 + W), or 0.
 int gemv_override();
 
+// Convolution kernel pinned by the override: 0 none, 1 the LDS-staged
+// four-wave kernel, 2 the register-direct one.
+int conv_override();
+
 // Element formats, same numbering as tmm_dtype in include/tmm.h.
 enum Fmt : int { kF32 = 0, kBF16 = 1, kF16 = 2, kF8 = 3 };
 
