@@ -243,7 +243,7 @@ int tmm_version(void);
  *   skinny=<bm>x<bn>   skinny-M tile, bm and bn in {16, 32, 64}
  *   gemv=<r>x<w>       GEMV rows per wave (1, 2, 4) and waves per workgroup
  *                      (4, 8, 16)
- *   conv=quad | direct the convolution kernel: LDS-staged 256-pixel x
+ *   conv=quad | direct the convolution kernel: LDS-staged 128-pixel x
  *                      128-filter tiles (taken only where C % 32 == 0 and
  *                      R S C >= 96) or register-direct 128/256 x 64 tiles
  * The same text in the environment variable TMM_OVERRIDE is read once, at

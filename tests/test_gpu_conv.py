@@ -52,8 +52,12 @@ def run(tmm, N, H, W, C, K, R, S, pad, fmt, out, relu, pool, seed, dist="uniform
           what=what)
 
 
-def test_listing_problem(tmm):
-    """The conv_fused listing's problem, bf16 inputs, fp32 output as there."""
+def test_listing_problem(tmm, force):
+    """The conv_fused listing's problem, bf16 inputs, fp32 output as there,
+    through the automatic choice (the LDS-staged kernel) and the
+    register-direct kernel."""
+    run(tmm, 8, 64, 64, 32, 64, 3, 3, 1, "bf16", "f32", True, 2, seed=2000)
+    force(conv="direct")
     run(tmm, 8, 64, 64, 32, 64, 3, 3, 1, "bf16", "f32", True, 2, seed=2000)
 
 
@@ -91,7 +95,7 @@ def test_without_scale_and_bias(tmm):
     run(tmm, 2, 8, 8, 16, 32, 3, 3, 1, "bf16", "f32", False, 1, seed=2300, scale=False, bias=False)
 
 
-# Channel counts that are multiples of 32, for the LDS-staged kernel (256
+# Channel counts that are multiples of 32, for the LDS-staged kernel (128
 # pixels x 128 filters per workgroup, one tap per 32-channel K-step):
 # pixels and filters that end mid-tile, two filter tiles, R != S with wide
 # padding, an odd step count (padded with a zero step), the fewest steps it
@@ -123,7 +127,7 @@ def test_lds_staged_kernel_integer_exact(tmm, force):
 
 
 def test_lds_staged_kernel_is_chosen_for_full_grids(tmm):
-    """16 x 64 x 64 pixels, C = 32: 256 workgroups of 256 x 128, enough for
+    """16 x 64 x 64 pixels, C = 32: 512 workgroups of 128 x 128, enough for
     the automatic choice to be the LDS-staged kernel (no override)."""
     run(tmm, 16, 64, 64, 32, 128, 3, 3, 1, "bf16", "bf16", True, 2, seed=2700)
 

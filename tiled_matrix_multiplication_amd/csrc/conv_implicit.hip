@@ -246,14 +246,14 @@ __global__ __launch_bounds__(256, 2) void conv_implicit_kernel(ConvParams p) {
 //
 // The LDS-staged kernel of conv_quad.h takes channel counts C % 32 == 0
 // (one tap per K-step) with R S C >= 96 (at least 4 steps) when its
-// 256 x 128 tiles fill every CU at least once.
+// 128 x 128 tiles give every CU one: the listing's problem (256 tiles)
+// 8.2 us against 9.9 us here.
 template <int AB, int CT>
 hipError_t launch_typed(const ConvParams &p, hipStream_t stream) {
   const int64_t P = p.H + 2 * p.pad - p.R + 1, Q = p.W + 2 * p.pad - p.S + 1;
   const int ov = conv_override();
   const bool quad_ok = p.C % 32 == 0 && (int64_t)p.R * p.S * p.C >= 96;
-  const int64_t quad_tiles = ((p.N * P * Q + 255) / 256) * ((p.K + 127) / 128);
-  if (quad_ok && (ov == 1 || (ov == 0 && quad_tiles >= (int64_t)device_cu_count())))
+  if (quad_ok && (ov == 1 || (ov == 0 && gemm_detail::conv_quad_tiles(p) >= (int64_t)device_cu_count())))
     return gemm_detail::launch_conv_quad<AB, CT>(p, stream);
   const int64_t tn = (p.K + kBN - 1) / kBN;
   const int64_t t256 = ((p.N * P * Q + 255) / 256) * tn;

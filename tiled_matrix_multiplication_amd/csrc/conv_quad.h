@@ -10,10 +10,14 @@
 // wave loading its own filter pieces; here a workgroup stages both operands
 // in LDS, as the four-wave GEMM does (gemm_quad.h), so every piece is
 // fetched once per workgroup and read by two waves:
-//   * a workgroup computes 256 pixels x 128 filters, four waves of 128 x 64
-//     (8 x 4 blocks of v_mfma_f32_16x16x32), in K-steps of 32 (r, s, c)
+//   * a workgroup computes 128 pixels x 128 filters, four waves of 64 x 64
+//     (4 x 4 blocks of v_mfma_f32_16x16x32), in K-steps of 32 (r, s, c)
 //     elements; with C % 32 == 0 one step lies within one tap (r, s) and
-//     covers channels 32 cb .. 32 cb + 31;
+//     covers channels 32 cb .. 32 cb + 31.  Its four stages take 64 KiB of
+//     LDS, so two workgroups share a CU and one's prologue and epilogue
+//     (a 3 x 3 tap over 64 channels is only 18 steps) overlap the other's
+//     matrix work: 64 x 64^2 x 64 -> 128, 3 x 3, pooled, 59.3 us against
+//     73.3 us with one workgroup of 256 x 128 per CU;
 //   * the im2col rows are never built: a stage row is one output pixel's 64
 //     bytes of the step, filled by direct 16-byte global->LDS loads whose
 //     per-lane source is the pixel's tap neighbour (y + r - pad,
@@ -21,7 +25,7 @@
 //     the weights are K-contiguous rows, loaded as the GEMM loads a
 //     K-contiguous B;
 //   * the ring, the swizzle, the fragment reads and the step schedule are
-//     those of gemm_quad.h on a 256 x 128 tile (loads three steps ahead, one
+//     those of gemm_quad.h (loads three steps ahead, one
 //     barrier per step, next step's fragments read during the current one);
 //     R S C / 32 steps are padded to an even count with all-zero steps;
 //   * with pooling the GEMM rows are ordered window by window (4
@@ -61,15 +65,15 @@ __device__ __forceinline__ void conv_pixel(int64_t m, int pool, int64_t P, int64
 }
 
 template <int AB, int CT>
-__global__ __launch_bounds__(256) void conv_quad_kernel(ConvParams p) {
-  constexpr int BM = 256, BN = 128, NW = 4;
+__global__ __launch_bounds__(256, 2) void conv_quad_kernel(ConvParams p) {
+  constexpr int BM = 128, BN = 128, NW = 4;
   constexpr int WTM = BM / 2, WTN = BN / 2;    // each wave's block
-  constexpr int FM = WTM / 16, FN = WTN / 16;  // 8 x 4 accumulators
+  constexpr int FM = WTM / 16, FN = WTN / 16;  // 4 x 4 accumulators
   constexpr int ROWB = kRingRowBytes;          // 64 bytes of a step per row
   constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int S = kRingStages;               // 4
-  constexpr int LA = A_BYTES / 1024 / NW;      // direct loads per wave per step: 4 (pixels)
+  constexpr int LA = A_BYTES / 1024 / NW;      // direct loads per wave per step: 2 (pixels)
   constexpr int LB = B_BYTES / 1024 / NW;      // 2 (filters)
   constexpr int LPS = LA + LB;
   static_assert(LPS <= FM, "one direct load per row block at most");
@@ -274,12 +278,16 @@ __global__ __launch_bounds__(256) void conv_quad_kernel(ConvParams p) {
   }
 }
 
-// 256 x 128 tiles; the host has checked C % 32 == 0 and R S C >= 96.
+// Workgroups of the LDS-staged kernel for a problem.
+inline int64_t conv_quad_tiles(const ConvParams &p) {
+  const int64_t P = p.H + 2 * p.pad - p.R + 1, Q = p.W + 2 * p.pad - p.S + 1;
+  return ((p.N * P * Q + 127) / 128) * ((p.K + 127) / 128);
+}
+
+// The host has checked C % 32 == 0 and R S C >= 96.
 template <int AB, int CT>
 hipError_t launch_conv_quad(const ConvParams &p, hipStream_t stream) {
-  const int64_t P = p.H + 2 * p.pad - p.R + 1, Q = p.W + 2 * p.pad - p.S + 1;
-  const int64_t tiles = ((p.N * P * Q + 255) / 256) * ((p.K + 127) / 128);
-  hipLaunchKernelGGL((conv_quad_kernel<AB, CT>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((conv_quad_kernel<AB, CT>), dim3((unsigned)conv_quad_tiles(p)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
