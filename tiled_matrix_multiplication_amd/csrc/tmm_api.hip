@@ -270,12 +270,13 @@ tmm::Tile pick_tile(int64_t M, int64_t N, int64_t batch, int ab) {
   const int cus = cu_count();
   // One 128-column panel (N <= 128) with a long K, e.g. attention's P . V:
   // the product streams A from HBM and every tile shape reads the same
-  // bytes, so the choice is occupancy.  128x128 tiles (64 KiB of LDS) run
-  // two workgroups per CU, so one tile's epilogue and prologue overlap the
-  // other's loads; with at least two such tiles per CU they measured 11 %
-  // faster than 256x128 (batch 128, 2048 x 128 x 2048 fp16: 226 vs 253 us).
+  // bytes.  For 16-bit inputs the four-wave kernel on 256x128 tiles streams
+  // fastest (batch 128, 2048 x 128 x 2048 fp16, one box: 222 us against 235
+  // on its 128x128 tiles, 243 on the two-stage 128x128 and 260 on the
+  // two-stage 256x128; a six-stage ring on 256x128 gained nothing); the
+  // others keep the two-stage 128x128 tiles, two workgroups per CU.
   if (N <= 128 && ab != TMM_F8E4M3 && ((M + 127) / 128) * batch >= 2 * (int64_t)cus)
-    return tmm::kTile128x128;
+    return (ab == TMM_BF16 || ab == TMM_F16) ? tmm::kTile256x128q : tmm::kTile128x128;
   const double eff[tmm::kNumAutoTiles] = {1.0, 0.85, 0.65};
   tmm::Tile best = tmm::kTile128x128;
   double best_cost = 1e300;
