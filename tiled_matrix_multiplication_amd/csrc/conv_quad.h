@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256, 2) void conv_quad_kernel(ConvParams p) {
 
   // ---- direct-load sources.  Load q of wave w fills stage rows
   // w BM/4 + 16 q .. +15 (A) or w BN/4 + 16 q (B); lane L lands at row
-  // L / 4, position L % 4 and loads logical chunk (L % 4) ^ swz64(row).
+  // L / 4, position L % 4 and loads logical chunk (L % 4) ^ qswz64(row).
   // A: the lane's pixel (rows past Mg take the last pixel; not stored).
   int64_t a_pix[LA];   // byte offset of pixel (n, y, x), channel 0, plus the chunk
   int a_y[LA], a_x[LA];
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void conv_quad_kernel(ConvParams p) {
     conv_pixel(min64(m0 + row, Mg - 1), p.pool, P, Q, OH, OW, n, y, x);
     a_y[q] = y;
     a_x[q] = x;
-    a_pix[q] = ((n * H + y) * W + x) * C * 2 + (((lane & 3) ^ swz64(row)) << 4);
+    a_pix[q] = ((n * H + y) * W + x) * C * 2 + (((lane & 3) ^ qswz64(row)) << 4);
   }
   // B: filter rows (past K: the last filter; not stored).
   const char *b_row[LB];
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256, 2) void conv_quad_kernel(ConvParams p) {
   for (int q = 0; q < LB; ++q) {
     const int row = wave * (BN / NW) + q * 16 + (lane >> 2);
     const int64_t f = min64(n0 + row, KF - 1);
-    b_row[q] = (const char *)p.w + f * Kg * 2 + (((lane & 3) ^ swz64(row)) << 4);
+    b_row[q] = (const char *)p.w + f * Kg * 2 + (((lane & 3) ^ qswz64(row)) << 4);
   }
   const uint32_t lds0 = lds_addr(lds);
 
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256, 2) void conv_quad_kernel(ConvParams p) {
   // ---- fragment addresses (bytes within a stage): row block base + lane
   // row l16, chunk G (swizzled)
   const int l16 = lane & 15, G = lane >> 4;
-  const int a_lane = l16 * ROWB + ((G ^ ((l16 >> 2) & 3)) << 4);
+  const int a_lane = l16 * ROWB + ((G ^ qswz64(l16)) << 4);
   const int a_base = wm * WTM * ROWB + a_lane;                   // + 1024 i
   const int b_base = A_BYTES + wn * WTN * ROWB + a_lane;         // + 1024 j
 
