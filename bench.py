@@ -94,6 +94,9 @@ WORKLOADS = {
     "skinny_m16": (16, 4096, 4096, 1, "f16", "f16", True, True),
     "skinny_m64": (64, 4096, 4096, 1, "f16", "f16", True, True),
     "skinny_m256": (256, 4096, 4096, 1, "f16", "f16", True, True),
+    # the same layer through tmm_gemm_splitk (K in 4 slices, workspace
+    # allocated outside the timed region); slices in SPLITK below
+    "skinny_m256_splitk": (256, 4096, 4096, 1, "f16", "f16", True, True),
     # full BLAS form (tmm_gemm_ex), options in FULL_FORM below
     "ffn_up_relu": (8192, 14336, 4096, 1, "bf16", "bf16", True, True),
     "ffn_down_residual": (8192, 4096, 14336, 1, "bf16", "bf16", True, True),
@@ -107,6 +110,9 @@ WORKLOADS = {
 }
 
 ATTENTION = ("attn_fused",)
+
+# Split-K workloads: K slices of tmm_gemm_splitk.
+SPLITK = {"skinny_m256_splitk": 4}
 
 # Fused stride-1 convolutions (NHWC): the conv_fused listing's problem of the
 # Lecture 27 notes (batch 8, 64 x 64, 32 -> 64 channels, 3 x 3, one-pixel
@@ -174,7 +180,8 @@ def describe(name):
     if name in ATTENTION:
         return (f"{fin} fused attention softmax(Q K^T/sqrt(D)) V, batch x heads {Z}, "
                 f"{M} queries x {N} keys, head size {K}, {fout} out")
-    return f"{fin} GEMM {b}{M}x{N}x{K} {lay}, {fout} out{', fp32 bias' if bias else ''}"
+    sk = f", split-K {SPLITK[name]}" if name in SPLITK else ""
+    return f"{fin} GEMM {b}{M}x{N}x{K} {lay}, {fout} out{', fp32 bias' if bias else ''}{sk}"
 
 
 def make_inputs(name, copies, dev):
@@ -275,6 +282,15 @@ def launcher(name, sets, dbias, sa, sb):
         def run(i):
             W, x, y = sets[i % len(sets)]
             tmm.tmm_gemv(W, x.view(-1)[:K], y.view(-1), bias=dbias)
+    elif name in SPLITK:
+        import torch
+        S = SPLITK[name]
+        ws = torch.empty(tmm.splitk_workspace_bytes(M, N, S) // 4, dtype=torch.float32,
+                         device=sets[0][0].device)
+
+        def run(i):
+            A, B, C = sets[i % len(sets)]
+            tmm.tmm_gemm_splitk(A, B, C, bias=dbias, trans_b=tb, splits=S, workspace=ws)
     elif Z > 1:
         def run(i):
             A, B, C = sets[i % len(sets)]
@@ -563,6 +579,9 @@ KERNEL_SOURCES = {
     "skinny": ["gemm_skinny.hip"],
     "attention": ["attention.hip"],
     "conv": ["conv_implicit.hip", "conv_quad.h", "gemm_quad.h", "gemm_ring.h", "gemm_mfma.h"],
+    "splitk": ["gemm_mfma.h", "gemm_ring.h", "gemm_quad.h", "gemm_quad8.h", "load_words.h", "gemm_f32.hip",
+               "gemm_bf16.hip", "gemm_f16.hip", "gemm_f8.hip", "gemm_ring_ta.hip", "gemm_short_k.hip",
+               "splitk.hip"],
 }
 
 
@@ -576,6 +595,8 @@ def kernel_family(name):
         return "gemv"
     if name in ATTENTION:
         return "attention"
+    if name in SPLITK:
+        return "splitk"
     if name.startswith("skinny"):
         return "gemv" if WORKLOADS[name][0] <= GEMV_MULTI_MAX_M else "skinny"
     if name in CONV:
@@ -623,12 +644,17 @@ def summarize_pmc(name, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, co
         kernel_substr = "gemv"
     elif name in ATTENTION:
         kernel_substr = "attn_fwd"
+    elif name in SPLITK:
+        kernel_substr = "gemm_"   # the partial products; the sum kernel is added below
     elif name.startswith("skinny"):
         kernel_substr = "gemm_skinny"
     elif name in CONV:
         kernel_substr = "conv_"   # conv_implicit_kernel or conv_quad_kernel
     f_k, nf = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", kernel_substr)
     w_k, nw = _counter_per_dispatch(write_csv, "WRITE_SIZE", kernel_substr)
+    if name in SPLITK:   # one call = the partial-product kernel + the sum kernel
+        f_k += _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "splitk_reduce")[0]
+        w_k += _counter_per_dispatch(write_csv, "WRITE_SIZE", "splitk_reduce")[0]
     f_c, _ = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", copy_substr)
     w_c, _ = _counter_per_dispatch(copy_write_csv, "WRITE_SIZE", copy_substr)
     fetch_scale = copy_bytes / f_c     # bytes per counter unit, from the copy's reads

@@ -93,7 +93,9 @@ enum tmm_status {
   TMM_ERR_STRIDE = -6, /* negative batch stride, or C matrices that overlap   */
   TMM_ERR_ALIGN = -7,  /* pointer not aligned to its element size            */
   TMM_ERR_LAUNCH = -8, /* HIP reported an error at launch                     */
-  TMM_ERR_ARG = -9     /* unknown activation code or pooling factor          */
+  TMM_ERR_ARG = -9,    /* unknown activation code or pooling factor, or a    */
+                       /* split count outside 1..64 or not dividing K        */
+  TMM_ERR_WORKSPACE = -10 /* workspace missing, too small or misaligned      */
 };
 
 /* Activation applied last by tmm_gemm_ex. */
@@ -220,6 +222,34 @@ int tmm_conv2d_fused(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int6
                      int64_t pad, tmm_dtype in_type, tmm_dtype out_type, const void *in,
                      const void *w, const float *scale, const float *bias, int activation,
                      int pool, void *out, hipStream_t stream);
+
+/*
+ * The product of tmm_gemm with K cut into `splits` equal slices, for
+ * products with few rows (the decode end of the batch-size table on the
+ * "GEMM to FlashAttention" page, where a one-pass tiling gives every CU its
+ * own long stretch of both operands): slice s's fp32 partial product goes to
+ * the caller's workspace, then the slices are summed and finished:
+ *
+ *   W[s] = A[:, s*K/S .. (s+1)*K/S) . op(B)[s*K/S .. (s+1)*K/S, :]   (fp32)
+ *   C    = round( scale_a*scale_b * (W[0] + W[1] + ... + W[S-1]) + bias )
+ *
+ * (S = splits), summed in that fixed order with one nearest-even rounding:
+ * the result is deterministic and within the fp32 summation bound of the
+ * one-pass product (the bias and scale as in tmm_gemm, the GEMM page's
+ * linear-layer formula and interface box).
+ *   splits    : 1 .. 64 dividing K (TMM_ERR_ARG); splits == 1 or K == 0 is
+ *               the one-pass product and leaves the workspace untouched
+ *   workspace : device memory of at least splits*M*N*4 bytes, 16-byte
+ *               aligned, owned by the caller and overlapping no operand
+ *               (TMM_ERR_WORKSPACE when NULL, smaller or misaligned); its
+ *               contents on return are unspecified.  Calls that share one
+ *               workspace must be ordered (same stream, or synchronised).
+ * Every other argument, type pair, limit and error as for tmm_gemm.
+ */
+int tmm_gemm_splitk(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type, tmm_dtype c_type,
+                    int trans_b, const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+                    int64_t ldc, const float *bias, float scale_a, float scale_b, int splits,
+                    void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /* Static English text of a status code (never NULL). */
 const char *tmm_status_string(int status);

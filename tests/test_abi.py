@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemm_ex", "tmm_gemv", "tmm_attention_fwd",
-         "tmm_conv2d_fused", "tmm_status_string", "tmm_version", "tmm_set_override"])
+         "tmm_conv2d_fused", "tmm_gemm_splitk", "tmm_status_string", "tmm_version", "tmm_set_override"])
 
 
 def test_library_exports_every_declared_symbol(tmm):
@@ -44,7 +44,7 @@ def declared_status_codes():
 def test_version_and_status_strings(tmm):
     assert tmm.tmm_version() == 10000
     codes = declared_status_codes()
-    assert sorted(codes) == list(range(-9, 1))
+    assert sorted(codes) == list(range(-10, 1))
     for code in codes:
         s = tmm.tmm_status_string(code)
         assert s and s != "unknown status code", code
@@ -227,6 +227,34 @@ def test_conv_validation(tmm):
     assert conv(tmm, H=0) == -1
     assert conv(tmm, x=None) == -3
     assert conv(tmm, x=ctypes.c_void_p(0x100008)) == -7   # input not 16-byte aligned
+
+
+def splitk(tmm, M=256, N=512, K=1024, ab=2, c=2, tb=1, A=FAKE, lda=None, B=FAKE2, ldb=None, C=FAKE3,
+           ldc=None, bias=None, splits=4, ws=ctypes.c_void_p(0x400000), ws_bytes=None):
+    lda = K if lda is None else lda
+    ldb = (K if tb else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    ws_bytes = splits * M * N * 4 if ws_bytes is None else ws_bytes
+    return tmm.lib.tmm_gemm_splitk(M, N, K, ab, c, tb, A, lda, B, ldb, C, ldc, bias, 1.0, 1.0, splits,
+                                   ws, ws_bytes, None)
+
+
+def test_splitk_arguments_checked_on_host(tmm):
+    """Split counts, the workspace and the usual GEMM checks, all before any
+    HIP call (the fake pointers are never dereferenced)."""
+    assert splitk(tmm, splits=0) == -9
+    assert splitk(tmm, splits=65) == -9
+    assert splitk(tmm, K=1000, splits=3) == -9               # 3 does not divide K
+    assert splitk(tmm, ws=None) == -10
+    assert splitk(tmm, ws_bytes=4 * 256 * 512 * 4 - 1) == -10
+    assert splitk(tmm, ws=ctypes.c_void_p(0x400008)) == -10   # not 16-byte aligned
+    assert splitk(tmm, lda=10) == -2
+    assert splitk(tmm, ab=1, c=2) == -4
+    assert splitk(tmm, A=None) == -3
+    assert splitk(tmm, M=-1) == -1
+    # quick returns: nothing to compute, nothing checked about the workspace
+    assert splitk(tmm, M=0, ws=None) == 0
+    assert splitk(tmm, N=0, ldc=1, ws=None) == 0
 
 
 def test_conv_quick_return(tmm):

@@ -22,11 +22,11 @@ TMM_F32, TMM_BF16, TMM_F16, TMM_F8E4M3 = 0, 1, 2, 3
 STATUS = {
     0: "TMM_OK", -1: "TMM_ERR_DIM", -2: "TMM_ERR_LD", -3: "TMM_ERR_NULL", -4: "TMM_ERR_DTYPE",
     -5: "TMM_ERR_SCALE", -6: "TMM_ERR_STRIDE", -7: "TMM_ERR_ALIGN", -8: "TMM_ERR_LAUNCH",
-    -9: "TMM_ERR_ARG",
+    -9: "TMM_ERR_ARG", -10: "TMM_ERR_WORKSPACE",
 }
 
 EXPORTS = ("tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemm_ex", "tmm_gemv", "tmm_attention_fwd",
-           "tmm_conv2d_fused",
+           "tmm_conv2d_fused", "tmm_gemm_splitk",
            "tmm_status_string", "tmm_version", "tmm_set_override")
 
 _DTYPE = {torch.float32: TMM_F32, torch.bfloat16: TMM_BF16, torch.float16: TMM_F16,
@@ -55,12 +55,14 @@ def _load() -> ctypes.CDLL:
                                 i64, i64, vp, cf, cf, ci, vp]
     lib.tmm_attention_fwd.argtypes = [i64, i64, i64, i64, ci, ci, vp, i64, i64, vp, i64, i64,
                                       vp, i64, i64, vp, i64, i64, cf, vp]
+    lib.tmm_gemm_splitk.argtypes = [i64, i64, i64, ci, ci, ci, vp, i64, vp, i64, vp, i64, vp, cf, cf, ci,
+                                    vp, i64, vp]
     lib.tmm_status_string.argtypes = [ci]
     lib.tmm_status_string.restype = ctypes.c_char_p
     lib.tmm_version.argtypes = []
     lib.tmm_set_override.argtypes = [ctypes.c_char_p]
     for f in (lib.tmm_gemm, lib.tmm_gemm_strided_batched, lib.tmm_gemm_ex, lib.tmm_gemv,
-              lib.tmm_attention_fwd, lib.tmm_conv2d_fused,
+              lib.tmm_attention_fwd, lib.tmm_conv2d_fused, lib.tmm_gemm_splitk,
               lib.tmm_version, lib.tmm_set_override):
         f.restype = ci
     return lib
@@ -140,6 +142,36 @@ def tmm_gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, bias: torch.Tens
                       _ld(B), _ptr(C), _ld(C), _ptr(bias), float(scale_a), float(scale_b),
                       ctypes.c_void_p(_stream(stream)))
     _check("tmm_gemm", rc)
+    return C
+
+
+def splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
+    """Workspace tmm_gemm_splitk needs: splits fp32 planes of M x N."""
+    return int(splits) * int(M) * int(N) * 4
+
+
+def tmm_gemm_splitk(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, bias: torch.Tensor | None = None,
+                    trans_b: bool = False, splits: int = 4, workspace: torch.Tensor | None = None,
+                    scale_a: float = 1.0, scale_b: float = 1.0, stream=None):
+    """C = scale_a*scale_b * A . op(B) (+ bias) with K cut into ``splits`` slices
+    whose fp32 partials go to ``workspace`` (a GPU tensor of at least
+    splitk_workspace_bytes(M, N, splits) bytes), then summed in order."""
+    _on_gpu(A, B, C, bias, workspace)
+    M, K = A.shape
+    N = B.shape[0] if trans_b else B.shape[1]
+    if (B.shape[1] if trans_b else B.shape[0]) != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    if B.dtype != A.dtype:
+        raise TypeError("A and B must have the same element type")
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (N,) or bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous float32 vector of N entries")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.tmm_gemm_splitk(M, N, K, _dtype(A), _dtype(C), int(bool(trans_b)), _ptr(A), _ld(A), _ptr(B),
+                             _ld(B), _ptr(C), _ld(C), _ptr(bias), float(scale_a), float(scale_b), int(splits),
+                             _ptr(workspace), ws_bytes, ctypes.c_void_p(_stream(stream)))
+    _check("tmm_gemm_splitk", rc)
     return C
 
 

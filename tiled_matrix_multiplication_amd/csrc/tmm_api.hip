@@ -84,6 +84,7 @@ struct Ex {
   int trans_a = 0;
   float beta = 0.f;
   int act = 0;
+  bool no_skinny = false;   // keep the product on the tiled kernels (split-K partials)
 };
 
 int check_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const void *A,
@@ -431,7 +432,7 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
       const int64_t cus = cu_count();
       const unsigned grid = (unsigned)std::max<int64_t>(8, std::min<int64_t>(total, cus) / 8 * 8);
       err = tmm::launch_gemm_short_k((Fmt)ab, p, grid, stream);
-    } else if (skinny_ok && (f == tmm::kTileSkinny || (f < 0 && M <= kSkinnyMaxM))) {
+    } else if (skinny_ok && !ex.no_skinny && (f == tmm::kTileSkinny || (f < 0 && M <= kSkinnyMaxM))) {
       int bm, bn;
       pick_skinny(M, N, batch, &bm, &bn);
       const int ce = elem_bytes(c);
@@ -450,6 +451,25 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
       err = dispatch_gemm(ab, c, trans_b != 0, tile, loads16, p, stream);
     }
   }
+  return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
+}
+
+// Split-K product (arguments checked by the caller): the K slices as one
+// batched fp32 product into W (slice s = batch entry s: A and B advanced by
+// K/S along K, W[s] dense M x N), kept off the skinny kernel so that the
+// tile choice sees S x the tiles, then the fixed-order sum with scale, bias
+// and one rounding (splitk.hip).
+int run_splitk(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const void *A,
+               int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc, const float *bias,
+               float scale_a, float scale_b, int splits, float *W, hipStream_t stream) {
+  Ex ex;
+  ex.no_skinny = true;
+  const int64_t ks = K / splits;
+  const int rc = run_gemm(M, N, ks, ab, TMM_F32, trans_b, A, lda, ks, B, ldb, trans_b ? ks : ks * ldb,
+                          W, N, M * N, splits, nullptr, 1.0f, 1.0f, stream, ex);
+  if (rc != TMM_OK) return rc;
+  const hipError_t err = tmm::launch_splitk_reduce((Fmt)c, M, N, splits, W, C, ldc, bias,
+                                                   scale_a * scale_b, stream);
   return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
 }
 
@@ -485,6 +505,27 @@ int tmm_gemm_strided_batched(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type,
                              float scale_a, float scale_b, hipStream_t stream) {
   return run_gemm(M, N, K, ab_type, c_type, trans_b, A, lda, strideA, B, ldb, strideB, C, ldc,
                   strideC, batch, bias, scale_a, scale_b, stream);
+}
+
+int tmm_gemm_splitk(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type, tmm_dtype c_type,
+                    int trans_b, const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+                    int64_t ldc, const float *bias, float scale_a, float scale_b, int splits,
+                    void *workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (splits < 1 || splits > 64) return TMM_ERR_ARG;
+  bool quick = false;
+  const int rc = check_gemm(M, N, K, ab_type, c_type, trans_b, A, lda, 0, B, ldb, 0, C, ldc, 0, 1,
+                            bias, scale_a, scale_b, Ex(), &quick);
+  if (rc != TMM_OK) return rc;
+  if (K % splits != 0) return TMM_ERR_ARG;
+  if (quick) return TMM_OK;
+  if (splits == 1 || K == 0)
+    return run_gemm(M, N, K, ab_type, c_type, trans_b, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, bias,
+                    scale_a, scale_b, stream);
+  // M * N < 2^62 / 256 here (check_gemm bounds the tiles), so no overflow
+  const int64_t need = (int64_t)splits * M * N * 4;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return TMM_ERR_WORKSPACE;
+  return run_splitk(M, N, K, ab_type, c_type, trans_b, A, lda, B, ldb, C, ldc, bias, scale_a,
+                    scale_b, splits, (float *)workspace, stream);
 }
 
 int tmm_gemv(int64_t N, int64_t K, tmm_dtype w_type, tmm_dtype y_type, const void *W,
@@ -596,7 +637,8 @@ const char *tmm_status_string(int status) {
     case TMM_ERR_STRIDE: return "negative batch stride or overlapping output matrices";
     case TMM_ERR_ALIGN: return "pointer not aligned to its element size";
     case TMM_ERR_LAUNCH: return "HIP reported an error at kernel launch";
-    case TMM_ERR_ARG: return "unknown activation code or pooling factor";
+    case TMM_ERR_ARG: return "unknown activation code or pooling factor, or a split count outside 1..64 or not dividing K";
+    case TMM_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     default: return "unknown status code";
   }
 }

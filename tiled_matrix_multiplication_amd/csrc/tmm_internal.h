@@ -101,6 +101,11 @@ hipError_t launch_gemm_short_k(Fmt ab, const GemmParams &p, unsigned grid, hipSt
 // empty sum.
 hipError_t launch_fill(Fmt c, const GemmParams &p, hipStream_t stream);
 
+// C[m][n] = round(scale * (W[0][m][n] + ... + W[S-1][m][n]) + bias[n]) for
+// fp32 partials W (S dense M x N planes) into C (ldc, format c) (splitk.hip).
+hipError_t launch_splitk_reduce(Fmt c, int64_t M, int64_t N, int S, const float *W, void *C,
+                                int64_t ldc, const float *bias, float scale, hipStream_t stream);
+
 struct GemvParams {
   int64_t N, K;
   const void *W;
