@@ -251,6 +251,24 @@ int tmm_gemm_splitk(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type, tmm_dtyp
                     int64_t ldc, const float *bias, float scale_a, float scale_b, int splits,
                     void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
+/*
+ * tmm_gemm_splitk without the workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The partial products go to a scratch
+ * array the library holds on each GPU it runs on, TMM_SPLITK_SCRATCH_BYTES
+ * (32 MiB) per GPU, kept until the process ends; this call allocates
+ * nothing.  A problem needing more than that (splits*M*N*4 bytes) returns
+ * TMM_ERR_WORKSPACE before any HIP call.  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap on a GPU (on concurrent streams or host
+ * threads) race and must be ordered by the caller.  Everything else as for
+ * tmm_gemm_splitk.
+ */
+#define TMM_SPLITK_SCRATCH_BYTES 33554432
+int tmm_gemm_splitk_noalloc(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type, tmm_dtype c_type,
+                            int trans_b, const void *A, int64_t lda, const void *B, int64_t ldb,
+                            void *C, int64_t ldc, const float *bias, float scale_a, float scale_b,
+                            int splits, hipStream_t stream);
+
 /* Static English text of a status code (never NULL). */
 const char *tmm_status_string(int status);
 

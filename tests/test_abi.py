@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemm_ex", "tmm_gemv", "tmm_attention_fwd",
-         "tmm_conv2d_fused", "tmm_gemm_splitk", "tmm_status_string", "tmm_version", "tmm_set_override"])
+         "tmm_conv2d_fused", "tmm_gemm_splitk", "tmm_gemm_splitk_noalloc", "tmm_status_string", "tmm_version",
+         "tmm_set_override"])
 
 
 def test_library_exports_every_declared_symbol(tmm):
@@ -255,6 +256,21 @@ def test_splitk_arguments_checked_on_host(tmm):
     # quick returns: nothing to compute, nothing checked about the workspace
     assert splitk(tmm, M=0, ws=None) == 0
     assert splitk(tmm, N=0, ldc=1, ws=None) == 0
+
+
+def test_splitk_noalloc_rejects_what_its_scratch_cannot_hold(tmm):
+    """The allocation-free variant checks on the host, before touching its
+    scratch: splits*M*N*4 above 32 MiB is TMM_ERR_WORKSPACE; the split checks
+    and quick returns are those of tmm_gemm_splitk."""
+    f = tmm.lib.tmm_gemm_splitk_noalloc
+    # 4 x 1024 x 2049 fp32 partials: 32 MiB + 16 KiB
+    assert f(1024, 2049, 4096, 2, 2, 1, FAKE, 4096, FAKE2, 4096, FAKE3, 2049, None, 1.0, 1.0, 4, None) == -10
+    assert f(256, 512, 1024, 2, 2, 1, FAKE, 1024, FAKE2, 1024, FAKE3, 512, None, 1.0, 1.0, 0, None) == -9
+    assert f(256, 512, 1000, 2, 2, 1, FAKE, 1000, FAKE2, 1000, FAKE3, 512, None, 1.0, 1.0, 3, None) == -9
+    assert f(0, 512, 1024, 2, 2, 1, FAKE, 1024, FAKE2, 1024, FAKE3, 512, None, 1.0, 1.0, 4, None) == 0
+    assert tmm.SPLITK_SCRATCH_BYTES == 32 << 20
+    header = open(HEADER).read()
+    assert re.search(r"#define TMM_SPLITK_SCRATCH_BYTES 33554432\b", header)
 
 
 def test_conv_quick_return(tmm):

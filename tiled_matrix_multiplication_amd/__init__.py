@@ -26,7 +26,7 @@ STATUS = {
 }
 
 EXPORTS = ("tmm_gemm", "tmm_gemm_strided_batched", "tmm_gemm_ex", "tmm_gemv", "tmm_attention_fwd",
-           "tmm_conv2d_fused", "tmm_gemm_splitk",
+           "tmm_conv2d_fused", "tmm_gemm_splitk", "tmm_gemm_splitk_noalloc",
            "tmm_status_string", "tmm_version", "tmm_set_override")
 
 _DTYPE = {torch.float32: TMM_F32, torch.bfloat16: TMM_BF16, torch.float16: TMM_F16,
@@ -57,12 +57,14 @@ def _load() -> ctypes.CDLL:
                                       vp, i64, i64, vp, i64, i64, cf, vp]
     lib.tmm_gemm_splitk.argtypes = [i64, i64, i64, ci, ci, ci, vp, i64, vp, i64, vp, i64, vp, cf, cf, ci,
                                     vp, i64, vp]
+    lib.tmm_gemm_splitk_noalloc.argtypes = [i64, i64, i64, ci, ci, ci, vp, i64, vp, i64, vp, i64, vp, cf, cf,
+                                            ci, vp]
     lib.tmm_status_string.argtypes = [ci]
     lib.tmm_status_string.restype = ctypes.c_char_p
     lib.tmm_version.argtypes = []
     lib.tmm_set_override.argtypes = [ctypes.c_char_p]
     for f in (lib.tmm_gemm, lib.tmm_gemm_strided_batched, lib.tmm_gemm_ex, lib.tmm_gemv,
-              lib.tmm_attention_fwd, lib.tmm_conv2d_fused, lib.tmm_gemm_splitk,
+              lib.tmm_attention_fwd, lib.tmm_conv2d_fused, lib.tmm_gemm_splitk, lib.tmm_gemm_splitk_noalloc,
               lib.tmm_version, lib.tmm_set_override):
         f.restype = ci
     return lib
@@ -172,6 +174,30 @@ def tmm_gemm_splitk(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, bias: tor
                              _ld(B), _ptr(C), _ld(C), _ptr(bias), float(scale_a), float(scale_b), int(splits),
                              _ptr(workspace), ws_bytes, ctypes.c_void_p(_stream(stream)))
     _check("tmm_gemm_splitk", rc)
+    return C
+
+
+SPLITK_SCRATCH_BYTES = 32 << 20   # TMM_SPLITK_SCRATCH_BYTES
+
+
+def tmm_gemm_splitk_noalloc(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                            bias: torch.Tensor | None = None, trans_b: bool = False, splits: int = 4,
+                            scale_a: float = 1.0, scale_b: float = 1.0, stream=None):
+    """tmm_gemm_splitk with the library's per-GPU scratch in place of a
+    workspace (no allocation; calls that overlap on one GPU race)."""
+    _on_gpu(A, B, C, bias)
+    M, K = A.shape
+    N = B.shape[0] if trans_b else B.shape[1]
+    if (B.shape[1] if trans_b else B.shape[0]) != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    if B.dtype != A.dtype:
+        raise TypeError("A and B must have the same element type")
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (N,) or bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous float32 vector of N entries")
+    rc = lib.tmm_gemm_splitk_noalloc(M, N, K, _dtype(A), _dtype(C), int(bool(trans_b)), _ptr(A), _ld(A),
+                                     _ptr(B), _ld(B), _ptr(C), _ld(C), _ptr(bias), float(scale_a),
+                                     float(scale_b), int(splits), ctypes.c_void_p(_stream(stream)))
+    _check("tmm_gemm_splitk_noalloc", rc)
     return C
 
 

@@ -454,6 +454,31 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
   return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
 }
 
+// Checks shared by the two split-K entry points; *done when the call is
+// complete without the split (a quick return, or splits == 1 / K == 0: the
+// one-pass product, enqueued here).
+int check_splitk(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const void *A,
+                 int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc, const float *bias,
+                 float scale_a, float scale_b, int splits, hipStream_t stream, bool *done) {
+  *done = false;
+  if (splits < 1 || splits > 64) return TMM_ERR_ARG;
+  bool quick = false;
+  const int rc = check_gemm(M, N, K, ab, c, trans_b, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, bias,
+                            scale_a, scale_b, Ex(), &quick);
+  if (rc != TMM_OK) return rc;
+  if (K % splits != 0) return TMM_ERR_ARG;
+  if (quick) {
+    *done = true;
+    return TMM_OK;
+  }
+  if (splits == 1 || K == 0) {
+    *done = true;
+    return run_gemm(M, N, K, ab, c, trans_b, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, bias, scale_a,
+                    scale_b, stream);
+  }
+  return TMM_OK;
+}
+
 // Split-K product (arguments checked by the caller): the K slices as one
 // batched fp32 product into W (slice s = batch entry s: A and B advanced by
 // K/S along K, W[s] dense M x N), kept off the skinny kernel so that the
@@ -471,6 +496,37 @@ int run_splitk(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, cons
   const hipError_t err = tmm::launch_splitk_reduce((Fmt)c, M, N, splits, W, C, ldc, bias,
                                                    scale_a * scale_b, stream);
   return err == hipSuccess ? TMM_OK : TMM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+// Scratch of tmm_gemm_splitk_noalloc: the split-K partial products of calls
+// that bring no workspace.  One copy per GPU (device memory of the code
+// object, zero-initialised at load, held until the process ends); nothing
+// in it needs to start at zero, as every call overwrites the partials it
+// reads.  Host code never uses this name as an address: scratch_address()
+// gives the current device's copy.
+constexpr int64_t kScratchBytes = TMM_SPLITK_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of this device's `scratch`, looked up with that device
+// current (hipGetSymbolAddress) at the first call on it and kept;
+// TMM_ERR_LAUNCH when the device or the lookup fails (tried again next call).
+int scratch_address(void **out) {
+  static std::mutex mu;
+  static void *addr[64] = {nullptr};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return TMM_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TMM_ERR_LAUNCH;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return TMM_OK;
 }
 
 }  // namespace
@@ -511,21 +567,32 @@ int tmm_gemm_splitk(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type, tmm_dtyp
                     int trans_b, const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
                     int64_t ldc, const float *bias, float scale_a, float scale_b, int splits,
                     void *workspace, int64_t workspace_bytes, hipStream_t stream) {
-  if (splits < 1 || splits > 64) return TMM_ERR_ARG;
-  bool quick = false;
-  const int rc = check_gemm(M, N, K, ab_type, c_type, trans_b, A, lda, 0, B, ldb, 0, C, ldc, 0, 1,
-                            bias, scale_a, scale_b, Ex(), &quick);
-  if (rc != TMM_OK) return rc;
-  if (K % splits != 0) return TMM_ERR_ARG;
-  if (quick) return TMM_OK;
-  if (splits == 1 || K == 0)
-    return run_gemm(M, N, K, ab_type, c_type, trans_b, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, bias,
-                    scale_a, scale_b, stream);
+  bool done = false;
+  const int rc = check_splitk(M, N, K, ab_type, c_type, trans_b, A, lda, B, ldb, C, ldc, bias,
+                              scale_a, scale_b, splits, stream, &done);
+  if (rc != TMM_OK || done) return rc;
   // M * N < 2^62 / 256 here (check_gemm bounds the tiles), so no overflow
   const int64_t need = (int64_t)splits * M * N * 4;
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return TMM_ERR_WORKSPACE;
   return run_splitk(M, N, K, ab_type, c_type, trans_b, A, lda, B, ldb, C, ldc, bias, scale_a,
                     scale_b, splits, (float *)workspace, stream);
+}
+
+int tmm_gemm_splitk_noalloc(int64_t M, int64_t N, int64_t K, tmm_dtype ab_type, tmm_dtype c_type,
+                            int trans_b, const void *A, int64_t lda, const void *B, int64_t ldb,
+                            void *C, int64_t ldc, const float *bias, float scale_a, float scale_b,
+                            int splits, hipStream_t stream) {
+  bool done = false;
+  const int rc = check_splitk(M, N, K, ab_type, c_type, trans_b, A, lda, B, ldb, C, ldc, bias,
+                              scale_a, scale_b, splits, stream, &done);
+  if (rc != TMM_OK || done) return rc;
+  const int64_t need = (int64_t)splits * M * N * 4;
+  if (need > kScratchBytes) return TMM_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != TMM_OK) return st;
+  return run_splitk(M, N, K, ab_type, c_type, trans_b, A, lda, B, ldb, C, ldc, bias, scale_a,
+                    scale_b, splits, (float *)ws, stream);
 }
 
 int tmm_gemv(int64_t N, int64_t K, tmm_dtype w_type, tmm_dtype y_type, const void *W,
