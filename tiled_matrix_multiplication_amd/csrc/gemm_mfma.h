@@ -850,8 +850,24 @@ hipError_t launch_one(const GemmParams &p, hipStream_t stream) {
 template <int AB, int CT, bool NT, int NW>
 hipError_t launch_ring(const GemmParams &p, hipStream_t stream);
 
-template <int AB, int CT, bool NT, int BM, int BN>
+template <int AB, int CT, bool NT, int BM, int BN, int TAIL>
 hipError_t launch_quad(const GemmParams &p, hipStream_t stream);
+
+// Whether the four-wave kernel applies to 16-bit inputs: its plain form
+// (TAIL = 0) takes an even number, at least 4, of 32-element K-steps with
+// whole 16-byte chunks in every row; its K-tail form (kQuadTail) any K whose
+// part below the last 64-element boundary short of K (short of K - 64 when
+// 64 divides K) holds at least 4 steps, including an NN B whose rows end
+// inside a chunk (N >= 8 for that one, so the chunk a row's end cuts through
+// has a next k-row to read into).
+template <bool NT>
+int quad_form(const GemmParams &p, int e) {
+  const bool cut = !NT && (p.N * e) % 16 != 0;
+  if (!cut && p.K % 64 == 0 && p.K >= 128) return 0;
+  const int64_t kt = p.K % 64 ? p.K % 64 : 64;
+  if (p.K - kt >= 128 && (!cut || p.N >= 8)) return 4;  // kQuadTail
+  return -1;
+}
 
 template <int CT, bool NT>
 hipError_t launch_quad8(const GemmParams &p, hipStream_t stream);
@@ -868,7 +884,7 @@ hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t str
         // kernels at every shape timed (4096^3 NN fp32 out 118.1 -> 102.3 us;
         // 8192x12288x4096 NT 661.6 -> 621.5 us; 8192^3 NN 880 -> 765 us).
         if constexpr (AB == kBF16 || AB == kF16) {
-          if (p.K % 64 == 0 && p.K >= 128) return launch_quad<AB, CT, NT, 256, 256>(p, stream);
+          if (quad_form<NT>(p, 2) == 0) return launch_quad<AB, CT, NT, 256, 256, 0>(p, stream);
         }
         // fp8: the four-wave kernel of gemm_quad8.h (an even number, at least
         // 4, of 64-element K-steps; the plain form): 8192^3 NN bf16 out
@@ -894,11 +910,17 @@ hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t str
         return launch_one<AB, CT, NT, 256, 256, 8, true>(p, stream);
       case kTile256x128q:
       case kTile128x128q:
-        // the four-wave kernel on narrower tiles (same conditions as above)
+        // the four-wave kernel on narrower tiles, in its plain or K-tail form
+        // (ragged 4097 x 511 x 1023 NN bf16: 39.6 us on the two-stage kernel)
         if constexpr (AB == kBF16 || AB == kF16) {
-          if (p.K % 64 == 0 && p.K >= 128) {
-            if (tile == kTile256x128q) return launch_quad<AB, CT, NT, 256, 128>(p, stream);
-            return launch_quad<AB, CT, NT, 128, 128>(p, stream);
+          const int form = quad_form<NT>(p, 2);
+          if (form == 0) {
+            if (tile == kTile256x128q) return launch_quad<AB, CT, NT, 256, 128, 0>(p, stream);
+            return launch_quad<AB, CT, NT, 128, 128, 0>(p, stream);
+          }
+          if (form > 0) {
+            if (tile == kTile256x128q) return launch_quad<AB, CT, NT, 256, 128, 4>(p, stream);
+            return launch_quad<AB, CT, NT, 128, 128, 4>(p, stream);
           }
         }
         if (tile == kTile256x128q) return launch_one<AB, CT, NT, 256, 128, 4, true>(p, stream);

@@ -1,6 +1,9 @@
 // Tiled GEMM on gfx950 matrix cores with four waves per 256x256 tile, each
-// wave owning a 128x128 block of C: the kernel for 16-bit inputs whose rows
-// are 16-byte aligned and whose K is a multiple of 64, at least 128.
+// wave owning a 128x128 block of C (or 256x128 / 128x128 tiles of four
+// waves): the kernel for 16-bit inputs, rows at any element alignment, whose
+// K is a multiple of 64, at least 128 -- or, in its K-tail form (kQuadTail),
+// any K with at least 128 below its last 64-element boundary, the last
+// elements of K read by words before the main loop.
 //
 //   C[z] = act(scale * A[z] . op(B[z]) (+ bias) (+ beta * old C[z])),
 //   row-major, z < batch, act = identity or ReLU
@@ -274,10 +277,16 @@ __device__ __forceinline__ void store_quad_ex(const f32x4 (&acc)[FM][FN], char *
   each_band(do_band, std::make_integer_sequence<int, FM / 2>());
 }
 
-// EPI: 0 the plain epilogue, 1 the plain one with ReLU, 2 the full form
-// (old C read back)
+// Flag in EPI selecting the K-tail form (see the prologue): K need not be a
+// multiple of 64, and an NN B's rows may end inside a 16-byte chunk.
+constexpr int kQuadTail = 4;
+
+// EPI, bits 0-1: 0 the plain epilogue, 1 the plain one with ReLU, 2 the
+// full form (old C read back); bit 2: kQuadTail.
 template <int AB, int CT, bool NT, int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
+  constexpr bool TAIL = (EPI & kQuadTail) != 0;
+  constexpr int EP = EPI & 3;
   constexpr int NW = 4;
   constexpr int WTM = BM / 2, WTN = BN / 2;     // each wave's block of C
   constexpr int FM = WTM / 16, FN = WTN / 16;   // 16x16 accumulators per wave
@@ -413,13 +422,96 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
     }
   };
 
-  const int64_t nsteps = K / BK;  // the host guarantees K % (2 BK) == 0, K >= 4 BK
-  constexpr int D = S - 1;        // steps loaded ahead
+  // K-tail form: the last KT elements of K (K mod 64, or 64 when that is 0)
+  // are not loaded by the ring; the host guarantees K - KT >= 4 BK.
+  const int64_t KT = TAIL ? ((K & 63) ? (K & 63) : 64) : 0;
+  const int64_t nsteps = (K - KT) / BK;  // the host guarantees an even count >= 4
+  constexpr int D = S - 1;               // steps loaded ahead
   auto stage_of = [](int64_t k) { return (int)(k & (S - 1)); };
   const int64_t pro = min64(D, nsteps);
-  for (int64_t k = 0; k < pro; ++k)
+  if constexpr (TAIL) {
+    // Steps 0 and 1 go out as usual.  The tail -- two 32-element steps from
+    // k0 = K - KT, zero past K, and for an NN B zero past N -- is read by
+    // words (load8_u16_words: only words holding a valid element, so no
+    // read leaves the operands), written to stages 2 and 3 in the ring's
+    // layout, and multiplied before the ring's first step; step 2's loads
+    // follow once every wave has read those stages.  The ring's loads then
+    // stay below k-row K - KT: whole chunks inside every row of A (and of a
+    // K-contiguous B), and for an NN B the chunk a row's end cuts through
+    // reads at most 7 elements into the next k-row (which exists, and holds
+    // N >= 8 elements, checked by the host); those columns past N feed
+    // only outputs that are never stored.
+    for (int64_t k = 0; k < 2; ++k)
 #pragma unroll
-    for (int q = 0; q < LPS; ++q) issue_one(k, (int)k, q);
+      for (int q = 0; q < LPS; ++q) issue_one(k, (int)k, q);
+    const int64_t k0 = K - KT;
+    constexpr int TQA = BM * 8 / 256;                      // tail chunks per thread (A)
+    constexpr int TQB = NT ? BN * 8 / 256 : 64 * CPR / 256;  // (B)
+    i32x4 ta[TQA], tb[TQB];
+#pragma unroll
+    for (int i = 0; i < TQA; ++i) {
+      const int q = tid + 256 * i, rr = q >> 3, c8 = q & 7;
+      const int64_t row = m0 + rr, k = k0 + 8 * c8;
+      const int nv = row < M ? (int)max64(0, min64(8, K - k)) : 0;
+      ta[i] = load8_u16_words(A + ((row < M ? row : 0) * p.lda + (k < K ? k : 0)) * E, nv);
+    }
+#pragma unroll
+    for (int i = 0; i < TQB; ++i) {
+      const int q = tid + 256 * i;
+      if constexpr (NT) {
+        const int rr = q >> 3, c8 = q & 7;
+        const int64_t row = n0 + rr, k = k0 + 8 * c8;
+        const int nv = row < N ? (int)max64(0, min64(8, K - k)) : 0;
+        tb[i] = load8_u16_words(B + ((row < N ? row : 0) * p.ldb + (k < K ? k : 0)) * E, nv);
+      } else {
+        const int kr = q / CPR, c = q % CPR;
+        const int64_t k = k0 + kr, col = n0 + 8 * c;
+        const int nv = k < K ? (int)max64(0, min64(8, N - col)) : 0;
+        tb[i] = load8_u16_words(B + ((k < K ? k : 0) * p.ldb + (col < N ? col : 0)) * E, nv);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TQA; ++i) {
+      const int q = tid + 256 * i, rr = q >> 3, c8 = q & 7;
+      *(i32x4 *)(lds + (2 + (c8 >> 2)) * STAGE + rr * ROWB + (((c8 & 3) ^ qswz64(rr)) << 4)) = ta[i];
+    }
+#pragma unroll
+    for (int i = 0; i < TQB; ++i) {
+      const int q = tid + 256 * i;
+      if constexpr (NT) {
+        const int rr = q >> 3, c8 = q & 7;
+        *(i32x4 *)(lds + (2 + (c8 >> 2)) * STAGE + A_BYTES + rr * ROWB + (((c8 & 3) ^ qswz64(rr)) << 4)) = tb[i];
+      } else {
+        const int kr = q / CPR, c = q % CPR, r32 = kr & 31;
+        *(i32x4 *)(lds + (2 + (kr >> 5)) * STAGE + A_BYTES + r32 * NB_ROW + ((c ^ qswz(r32)) << 4)) = tb[i];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (t == 1 && KT <= BK) break;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) read_a(2 + t, i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        read_b(2 + t, fb0, j, 0);
+        read_b(2 + t, fb0, j, 1);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mma16<AB>(fa[i], fb0[j], acc[i][j]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // every read of stages 2 and 3 done before they are reloaded
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) issue_one(2, 2, q);
+  } else {
+    for (int64_t k = 0; k < pro; ++k)
+#pragma unroll
+      for (int q = 0; q < LPS; ++q) issue_one(k, (int)k, q);
+  }
   // steps 0 and 1 landed (step 2 may still be in flight), then published
   if (pro > 2) __builtin_amdgcn_s_waitcnt(vm_wait(LPS));
   else __builtin_amdgcn_s_waitcnt(vm_wait(0));
@@ -476,28 +568,28 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
 
   // ---- epilogue (the loop's last barrier follows every LDS read of the stages)
   char *C = (char *)p.C + z * p.strideC * CE;
-  if constexpr (EPI == 2) {
+  if constexpr (EP == 2) {
     static_assert(NW * 32 * quad_ex_pitch<CT, FN>() <= S * STAGE, "epilogue staging");
     store_quad_ex<CT, FM, FN>(acc, lds + wave * 32 * quad_ex_pitch<CT, FN>(), C, p.ldc, M, N, m0 + wm * WTM,
                               n0 + wn * WTN, p.bias, p.scale, p.beta, p.act, lane);
   } else {
     static_assert(NW * 32 * quad_pitch<CT, FN>() <= S * STAGE, "epilogue staging");
-    store_quad<CT, FM, FN, EPI == 1>(acc, lds + wave * 32 * quad_pitch<CT, FN>(), C, p.ldc, M, N, m0 + wm * WTM,
+    store_quad<CT, FM, FN, EP == 1>(acc, lds + wave * 32 * quad_pitch<CT, FN>(), C, p.ldc, M, N, m0 + wm * WTM,
                            n0 + wn * WTN, p.bias, p.scale, lane);
   }
 }
 
-template <int AB, int CT, bool NT, int BM, int BN>
+template <int AB, int CT, bool NT, int BM, int BN, int TAIL>
 hipError_t launch_quad(const GemmParams &p, hipStream_t stream) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
   // each epilogue in its own instantiation, so the plain kernel's code is
   // what it was without the others; only beta != 0 reads the old C
   if (p.beta != 0.f)
-    hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN, 2>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN, 2 | TAIL>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
   else if (p.act == 1)
-    hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN, 1>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN, 1 | TAIL>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN, 0>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN, 0 | TAIL>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
