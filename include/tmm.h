@@ -294,6 +294,9 @@ int tmm_version(void);
  *   conv=quad | direct the convolution kernel: LDS-staged 128-pixel x
  *                      128-filter tiles (taken only where C % 32 == 0 and
  *                      R S C >= 96) or register-direct 128/256 x 64 tiles
+ *   ring=4 | 8         stages of the four-wave kernel's ring on 128x128
+ *                      tiles (8: plain epilogue and at least 8 ring steps
+ *                      only; chosen by the grid's size otherwise)
  * The same text in the environment variable TMM_OVERRIDE is read once, at
  * the library's first call (an unparsable value pins nothing).  This call
  * replaces the whole setting for every later call from any thread; calls

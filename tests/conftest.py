@@ -31,14 +31,14 @@ def pytest_collection_modifyitems(config, items):
 @pytest.fixture
 def force():
     """Pin the library's kernel choice for one test through tmm_set_override:
-    force(tile) / force(tile, skinny="<bm>x<bn>") / force(conv="quad") / force()
-    for the automatic choice; the automatic choice is restored when the test
-    ends."""
+    force(tile) / force(tile, skinny="<bm>x<bn>") / force(conv="quad") /
+    force(tile, ring=8) / force() for the automatic choice; the automatic
+    choice is restored when the test ends."""
     import tiled_matrix_multiplication_amd as t
 
-    def pin(tile=None, skinny=None, conv=None):
+    def pin(tile=None, skinny=None, conv=None, ring=None):
         items = ([f"tile={tile}"] if tile else []) + ([f"skinny={skinny}"] if skinny else []) + \
-                ([f"conv={conv}"] if conv else [])
+                ([f"conv={conv}"] if conv else []) + ([f"ring={ring}"] if ring else [])
         t.tmm_set_override(";".join(items) or None)
 
     yield pin

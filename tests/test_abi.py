@@ -283,10 +283,10 @@ def test_override_accepts_the_documented_keys_and_rejects_others(tmm):
     try:
         for spec in ["", "tile=128x128", "tile=skinny;skinny=32x64", "tile=gemvm", "gemv=2x16",
                      "tile=shortk skinny=16x16 gemv=1x4", "tile=generic", "tile=256x256r",
-                     "conv=quad", "conv=direct;tile=256x256q"]:
+                     "conv=quad", "conv=direct;tile=256x256q", "ring=8", "tile=128x128q;ring=4"]:
             assert tmm.lib.tmm_set_override(spec.encode()) == 0, spec
         for spec in ["tile=99x99", "skinny=8x16", "gemv=3x4", "gemv=2,16", "foo=1", "tile", "tile=128x128;x",
-                     "conv=fast"]:
+                     "conv=fast", "ring=6", "ring="]:
             assert tmm.lib.tmm_set_override(spec.encode()) == -9, spec
         assert tmm.lib.tmm_set_override(None) == 0
     finally:

@@ -1,13 +1,15 @@
 """GPU parity of the four-wave kernel's K-tail form (gemm_quad.h, kQuadTail)
-against the oracle: K not a multiple of 64, its last K mod 64 elements (one
-or two 32-element steps) read by words before the main loop, and NN B rows
-that end inside a 16-byte chunk (the last 64 k-rows read that way when 64
-divides K).  Each case runs on the 128x128 and 256x128 four-wave tiles and
-through the automatic choice; rows at 2-byte alignment (odd K or N, odd
-padding), ragged M and N, every output type, bias, the plain, ReLU and
-beta forms, batches, and small integers held bit for bit.  Shapes just
-outside the form (K - (K mod 64) < 128, or a cut NN row shorter than 8
-elements) take the two-stage kernel and are checked the same way."""
+and of its eight-stage ring on 128x128 tiles (kQuadDeep) against the
+oracle.  K-tail form: K not a multiple of 64, its last K mod 64 elements
+(one or two 32-element steps) read by words before the main loop, and NN B
+rows that end inside a 16-byte chunk (the last 64 k-rows read that way when
+64 divides K).  Each case runs on the 128x128 tiles with four and with eight
+ring stages, on the 256x128 tiles and through the automatic choice; rows at
+2-byte alignment (odd K or N, odd padding), ragged M and N, every output
+type, bias, the plain, ReLU and beta forms, batches, and small integers held
+bit for bit.  Shapes just outside a form (K - (K mod 64) < 128, fewer than 8
+ring steps for eight stages, a cut NN row shorter than 8 elements) take the
+next kernel down and are checked the same way."""
 import numpy as np
 import pytest
 import torch
@@ -20,7 +22,8 @@ from test_gpu_gemm_ex import run_case
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["128x128q", "256x128q", None]
+# (tile, ring stages): None = the automatic choice
+TILES = [("128x128q", 4), ("128x128q", 8), ("256x128q", None), (None, None)]
 
 # (M, N, K, in, out, trans_b, dist, bias, pad)
 CASES = [
@@ -36,6 +39,10 @@ CASES = [
     (40, 100, 150, "f16", "f16", False, "normal", True, 5),      # K - KT = 128 exactly
     (33, 7, 256, "bf16", "bf16", False, "normal", True, 0),      # cut row of 7: two-stage kernel
     (50, 100, 127, "bf16", "f32", True, "normal", False, 0),     # K - KT = 64: two-stage kernel
+    (300, 384, 256, "bf16", "f32", False, "normal", True, 0),    # 64 | K: 8 ring steps exactly
+    (260, 200, 261, "f16", "f16", True, "int", True, 0),         # tail of 5 after 8 ring steps
+    (130, 264, 2048, "bf16", "bf16", False, "normal", True, 0),  # 64 ring steps
+    (129, 136, 230, "bf16", "f32", False, "normal", False, 0),   # 6 ring steps: four stages only
 ]
 
 
@@ -51,13 +58,13 @@ def tmm():
 
 
 @pytest.mark.parametrize("case", CASES, ids=[_id(c) for c in CASES])
-def test_tail_form(tmm, case, force):
+def test_tail_and_ring_forms(tmm, case, force):
     M, N, K, fmt, out, tb, dist, bias, pad = case
-    for tile in TILES:
-        force(tile)
+    for tile, ring in TILES:
+        force(tile, ring=ring)
         dC, o, T = gemm_case(tmm, M, N, K, fmt, out, tb, dist, bias, seed=7000 + 10 * CASES.index(case),
                              pad=pad)
-        check(dC, o, T, K, exact=(dist == "int"), what=f"{_id(case)} tile {tile or 'auto'}")
+        check(dC, o, T, K, exact=(dist == "int"), what=f"{_id(case)} tile {tile or 'auto'} ring {ring}")
 
 
 @pytest.mark.parametrize("tile", ["128x128q", "256x128q"])
@@ -71,11 +78,12 @@ def test_tail_form_relu_and_beta(tmm, tile, tb, force):
              what=f"tail beta relu {tile}")
 
 
-def test_tail_form_batched(tmm, force):
+@pytest.mark.parametrize("ring", [4, 8])
+def test_tail_form_batched(tmm, force, ring):
     """Three batch entries with cut NN rows and a K tail: each entry's last
     k-rows are read by words, the rows before them reach into the next k-row
     of the same entry only."""
-    force("128x128q")
+    force("128x128q", ring=ring)
     Z, M, N, K = 3, 200, 250, 421
     A = syn.to_bits(syn.normal((Z, M, K), 7401), "bf16")
     B = syn.to_bits(syn.normal((Z, K, N), 7402), "bf16")
@@ -86,17 +94,18 @@ def test_tail_form_batched(tmm, force):
     torch.cuda.synchronize()
     for z in range(Z):
         o, T = oracle.gemm("bf16", A[z], B[z], bias=bvec, want_abs=True)
-        check(dC[z], o, T, K, what=f"batched tail z {z}")
+        check(dC[z], o, T, K, what=f"batched tail z {z} ring {ring}")
 
 
 def test_ragged_shape_takes_the_tail_form(tmm, force):
     """4097 x 511 x 1023 NN bf16 (cut rows, K tail of 63) on the automatic
     choice, every output against the oracle; and the same bits when the
-    128x128 four-wave tile is pinned (the automatic choice is that tile)."""
+    128x128 four-wave tile with eight stages is pinned (the automatic choice
+    for its one round of 132 tiles)."""
     force()
     M, N, K = 4097, 511, 1023
     dC, o, T = gemm_case(tmm, M, N, K, "bf16", "bf16", False, "normal", False, seed=7500)
     check(dC, o, T, K, what="ragged 4097x511x1023 tail form")
-    force("128x128q")
+    force("128x128q", ring=8)
     dC2, _, _ = gemm_case(tmm, M, N, K, "bf16", "bf16", False, "normal", False, seed=7500)
     assert torch.equal(dC.view(torch.int16), dC2.view(torch.int16))

@@ -853,6 +853,21 @@ hipError_t launch_ring(const GemmParams &p, hipStream_t stream);
 template <int AB, int CT, bool NT, int BM, int BN, int TAIL>
 hipError_t launch_quad(const GemmParams &p, hipStream_t stream);
 
+template <int AB, int CT, bool NT, int TAIL>
+hipError_t launch_quad_deep(const GemmParams &p, hipStream_t stream);
+
+// Whether the 128x128 four-wave tiles take the eight-stage ring: one round
+// of tiles (each CU streams its own panels, so seven steps in flight instead
+// of three hide more of the loads' latency), the plain epilogue, and at
+// least 8 ring steps; `kt` is the K-tail form's tail (0 in the plain form).
+// The override's ring=4 / ring=8 pins it either way where it applies.
+inline bool quad_deep(const GemmParams &p, int64_t kt) {
+  if (p.beta != 0.f || p.act != 0 || (p.K - kt) / 32 < 8) return false;
+  const int r = ring_override();
+  if (r) return r == 8;
+  return ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch <= device_cu_count();
+}
+
 // Whether the four-wave kernel applies to 16-bit inputs: its plain form
 // (TAIL = 0) takes an even number, at least 4, of 32-element K-steps with
 // whole 16-byte chunks in every row; its K-tail form (kQuadTail) any K whose
@@ -916,10 +931,12 @@ hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t str
           const int form = quad_form<NT>(p, 2);
           if (form == 0) {
             if (tile == kTile256x128q) return launch_quad<AB, CT, NT, 256, 128, 0>(p, stream);
+            if (quad_deep(p, 0)) return launch_quad_deep<AB, CT, NT, 0>(p, stream);
             return launch_quad<AB, CT, NT, 128, 128, 0>(p, stream);
           }
           if (form > 0) {
             if (tile == kTile256x128q) return launch_quad<AB, CT, NT, 256, 128, 4>(p, stream);
+            if (quad_deep(p, p.K % 64 ? p.K % 64 : 64)) return launch_quad_deep<AB, CT, NT, 4>(p, stream);
             return launch_quad<AB, CT, NT, 128, 128, 4>(p, stream);
           }
         }

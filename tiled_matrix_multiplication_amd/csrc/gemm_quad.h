@@ -93,6 +93,26 @@ __device__ __forceinline__ f32x4 mma16(const i32x4 &a, const i32x4 &b, const f32
 template <int CT, int FN>
 constexpr int quad_pitch() { return 16 * FN * FmtBytes<CT>::value + 16; }
 
+// 16 bytes to an address that is only element-aligned (rows of a C whose
+// pitch is not a multiple of 16 bytes): one 16-byte store where it is 4-byte
+// aligned, else a 2-byte store, three 4-byte stores and a 2-byte store, every
+// access naturally aligned (a 2-byte store per element took 2 us more on the
+// 4097 x 511 bf16 output).
+typedef int i32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ void store16_elem_aligned(char *dst, const i32x4 &v) {
+  if (((uintptr_t)dst & 3) == 0) {
+    *(i32x4_a4 *)dst = v;
+  } else {
+    const uint32_t w0 = (uint32_t)v[0], w1 = (uint32_t)v[1], w2 = (uint32_t)v[2], w3 = (uint32_t)v[3];
+    uint32_t *d = (uint32_t *)(dst + 2);
+    *(uint16_t *)dst = (uint16_t)w0;
+    d[0] = (w0 >> 16) | (w1 << 16);
+    d[1] = (w1 >> 16) | (w2 << 16);
+    d[2] = (w2 >> 16) | (w3 << 16);
+    *(uint16_t *)(dst + 14) = (uint16_t)(w3 >> 16);
+  }
+}
+
 template <int CT, int FM, int FN, bool RELU>
 __device__ __forceinline__ void store_quad(const f32x4 (&acc)[FM][FN], char *st, char *C, int64_t ldc,
                                            int64_t M, int64_t N, int64_t row0, int64_t col0,
@@ -141,6 +161,8 @@ __device__ __forceinline__ void store_quad(const f32x4 (&acc)[FM][FN], char *st,
       char *dst = C + (grow * ldc + gcol) * CE;
       if (vec && gcol + EPC <= N) {
         __builtin_nontemporal_store(v, (i32x4 *)dst);
+      } else if (gcol + EPC <= N) {
+        store16_elem_aligned(dst, v);
       } else {
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
@@ -175,7 +197,7 @@ struct OldQuad<kF32> { typedef f32x4 type; };
 // Calls f(integral_constant<int, 0>), f(..1), ... in order while it
 // returns true.
 template <typename F, int... I>
-__device__ __forceinline__ void each_band(F &f, std::integer_sequence<int, I...>) {
+__device__ __forceinline__ void for_each_index(F &f, std::integer_sequence<int, I...>) {
   (void)(... && f(std::integral_constant<int, I>()));
 }
 
@@ -274,18 +296,24 @@ __device__ __forceinline__ void store_quad_ex(const f32x4 (&acc)[FM][FN], char *
     __builtin_amdgcn_wave_barrier();
     return true;
   };
-  each_band(do_band, std::make_integer_sequence<int, FM / 2>());
+  for_each_index(do_band, std::make_integer_sequence<int, FM / 2>());
 }
 
 // Flag in EPI selecting the K-tail form (see the prologue): K need not be a
 // multiple of 64, and an NN B's rows may end inside a 16-byte chunk.
 constexpr int kQuadTail = 4;
+// Flag in EPI selecting an eight-stage ring (128x128 tiles): seven steps in
+// flight instead of three, for grids of one round of tiles, where each CU
+// streams its own operand panels and the loads' latency, not the matrix
+// work, sets the step time.
+constexpr int kQuadDeep = 8;
 
 // EPI, bits 0-1: 0 the plain epilogue, 1 the plain one with ReLU, 2 the
-// full form (old C read back); bit 2: kQuadTail.
+// full form (old C read back); bit 2: kQuadTail; bit 3: kQuadDeep.
 template <int AB, int CT, bool NT, int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   constexpr bool TAIL = (EPI & kQuadTail) != 0;
+  constexpr bool DEEP = (EPI & kQuadDeep) != 0;
   constexpr int EP = EPI & 3;
   constexpr int NW = 4;
   constexpr int WTM = BM / 2, WTN = BN / 2;     // each wave's block of C
@@ -297,14 +325,14 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   constexpr int A_BYTES = BM * ROWB;
   constexpr int B_BYTES = BN * ROWB;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int S = kRingStages;                // 4
+  constexpr int S = DEEP ? 8 : kRingStages;     // 4 (8)
   constexpr int NB_ROW = BN * E;                // NN: bytes of one k-row of the B stage
   constexpr int CPR = NB_ROW / 16, RPI = 64 / CPR;  // NN: chunks per k-row, k-rows per load
   constexpr int LA = A_BYTES / 1024 / NW;       // direct loads per wave per step (A)
   constexpr int LB = B_BYTES / 1024 / NW;       // (B)
   constexpr int LPS = LA + LB;
   static_assert(E == 2, "four-wave kernel: 16-bit inputs");
-  static_assert(S == 4 && BK == 32, "geometry");
+  static_assert((S == 4 || (S == 8 && BM == 128 && BN == 128)) && BK == 32, "geometry");
   static_assert((BM == 256 || BM == 128) && (BN == 256 || BN == 128) && FM >= FN, "tile shapes");
   static_assert(LPS <= FM, "one direct load per row block at most");
   // slots (instruction index within a row block) of the two B half-reads and the load
@@ -430,20 +458,23 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   auto stage_of = [](int64_t k) { return (int)(k & (S - 1)); };
   const int64_t pro = min64(D, nsteps);
   if constexpr (TAIL) {
-    // Steps 0 and 1 go out as usual.  The tail -- two 32-element steps from
-    // k0 = K - KT, zero past K, and for an NN B zero past N -- is read by
-    // words (load8_u16_words: only words holding a valid element, so no
-    // read leaves the operands), written to stages 2 and 3 in the ring's
-    // layout, and multiplied before the ring's first step; step 2's loads
-    // follow once every wave has read those stages.  The ring's loads then
-    // stay below k-row K - KT: whole chunks inside every row of A (and of a
-    // K-contiguous B), and for an NN B the chunk a row's end cuts through
-    // reads at most 7 elements into the next k-row (which exists, and holds
-    // N >= 8 elements, checked by the host); those columns past N feed
-    // only outputs that are never stored.
-    for (int64_t k = 0; k < 2; ++k)
-#pragma unroll
-      for (int q = 0; q < LPS; ++q) issue_one(k, (int)k, q);
+    // The tail -- two 32-element steps from k0 = K - KT, zero past K, and
+    // for an NN B zero past N -- is read first, one 16-byte load per chunk
+    // holding a valid element (load8_u16_tail: a chunk that K or N cuts is
+    // loaded from where its last valid element ends it and shifted into
+    // place, so no read leaves the operands: K - KT >= 128, and a cut NN row
+    // holds N >= 8 elements; five word loads per chunk instead cost 3.4 of
+    // the 22.6 us of 4097 x 511 x 1023 NN bf16); then the ring's first D
+    // steps go out as in the plain form, and the
+    // tail passes one step at a time through the last stage (which the
+    // ring's first step reloads), in the ring's layout, each published by a
+    // barrier, multiplied, and released by a second one.  Its loads' latency
+    // runs under the ring's.  The ring's loads stay below k-row K - KT:
+    // whole chunks inside every row of A (and of a K-contiguous B), and for
+    // an NN B the chunk a row's end cuts through reads at most 7 elements
+    // into the next k-row (which exists, and holds N >= 8 elements, checked
+    // by the host); those columns past N feed only outputs that are never
+    // stored.
     const int64_t k0 = K - KT;
     constexpr int TQA = BM * 8 / 256;                      // tail chunks per thread (A)
     constexpr int TQB = NT ? BN * 8 / 256 : 64 * CPR / 256;  // (B)
@@ -453,7 +484,7 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
       const int q = tid + 256 * i, rr = q >> 3, c8 = q & 7;
       const int64_t row = m0 + rr, k = k0 + 8 * c8;
       const int nv = row < M ? (int)max64(0, min64(8, K - k)) : 0;
-      ta[i] = load8_u16_words(A + ((row < M ? row : 0) * p.lda + (k < K ? k : 0)) * E, nv);
+      ta[i] = nv > 0 ? load8_u16_tail(A + (row * p.lda + k) * E, nv) : i32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < TQB; ++i) {
@@ -462,58 +493,62 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
         const int rr = q >> 3, c8 = q & 7;
         const int64_t row = n0 + rr, k = k0 + 8 * c8;
         const int nv = row < N ? (int)max64(0, min64(8, K - k)) : 0;
-        tb[i] = load8_u16_words(B + ((row < N ? row : 0) * p.ldb + (k < K ? k : 0)) * E, nv);
+        tb[i] = nv > 0 ? load8_u16_tail(B + (row * p.ldb + k) * E, nv) : i32x4{0, 0, 0, 0};
       } else {
         const int kr = q / CPR, c = q % CPR;
         const int64_t k = k0 + kr, col = n0 + 8 * c;
         const int nv = k < K ? (int)max64(0, min64(8, N - col)) : 0;
-        tb[i] = load8_u16_words(B + ((k < K ? k : 0) * p.ldb + (col < N ? col : 0)) * E, nv);
+        tb[i] = nv > 0 ? load8_u16_tail(B + (k * p.ldb + col) * E, nv) : i32x4{0, 0, 0, 0};
       }
     }
+    for (int64_t k = 0; k < pro; ++k)
 #pragma unroll
-    for (int i = 0; i < TQA; ++i) {
-      const int q = tid + 256 * i, rr = q >> 3, c8 = q & 7;
-      *(i32x4 *)(lds + (2 + (c8 >> 2)) * STAGE + rr * ROWB + (((c8 & 3) ^ qswz64(rr)) << 4)) = ta[i];
-    }
-#pragma unroll
-    for (int i = 0; i < TQB; ++i) {
-      const int q = tid + 256 * i;
-      if constexpr (NT) {
-        const int rr = q >> 3, c8 = q & 7;
-        *(i32x4 *)(lds + (2 + (c8 >> 2)) * STAGE + A_BYTES + rr * ROWB + (((c8 & 3) ^ qswz64(rr)) << 4)) = tb[i];
-      } else {
-        const int kr = q / CPR, c = q % CPR, r32 = kr & 31;
-        *(i32x4 *)(lds + (2 + (kr >> 5)) * STAGE + A_BYTES + r32 * NB_ROW + ((c ^ qswz(r32)) << 4)) = tb[i];
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-    __syncthreads();
+      for (int q = 0; q < LPS; ++q) issue_one(k, (int)k, q);
+    char *const ts = lds + (S - 1) * STAGE;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       if (t == 1 && KT <= BK) break;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) read_a(2 + t, i);
+      for (int i = 0; i < TQA; ++i) {
+        const int q = tid + 256 * i, rr = q >> 3, c8 = q & 7;
+        if ((c8 >> 2) == t) *(i32x4 *)(ts + rr * ROWB + (((c8 & 3) ^ qswz64(rr)) << 4)) = ta[i];
+      }
+#pragma unroll
+      for (int i = 0; i < TQB; ++i) {
+        const int q = tid + 256 * i;
+        if constexpr (NT) {
+          const int rr = q >> 3, c8 = q & 7;
+          if ((c8 >> 2) == t) *(i32x4 *)(ts + A_BYTES + rr * ROWB + (((c8 & 3) ^ qswz64(rr)) << 4)) = tb[i];
+        } else {
+          const int kr = q / CPR, c = q % CPR, r32 = kr & 31;
+          if ((kr >> 5) == t) *(i32x4 *)(ts + A_BYTES + r32 * NB_ROW + ((c ^ qswz(r32)) << 4)) = tb[i];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < FM; ++i) read_a(S - 1, i);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        read_b(2 + t, fb0, j, 0);
-        read_b(2 + t, fb0, j, 1);
+        read_b(S - 1, fb0, j, 0);
+        read_b(S - 1, fb0, j, 1);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = mma16<AB>(fa[i], fb0[j], acc[i][j]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // every read of the stage done before it is rewritten
+      __syncthreads();
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // every read of stages 2 and 3 done before they are reloaded
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < LPS; ++q) issue_one(2, 2, q);
   } else {
     for (int64_t k = 0; k < pro; ++k)
 #pragma unroll
       for (int q = 0; q < LPS; ++q) issue_one(k, (int)k, q);
   }
-  // steps 0 and 1 landed (step 2 may still be in flight), then published
-  if (pro > 2) __builtin_amdgcn_s_waitcnt(vm_wait(LPS));
+  // steps 0 and 1 landed (steps 2 .. D - 1 may still be in flight), then
+  // published; the eight-stage ring always has nsteps >= 8
+  if constexpr (DEEP) __builtin_amdgcn_s_waitcnt(vm_wait((D - 2) * LPS));
+  else if (pro > 2) __builtin_amdgcn_s_waitcnt(vm_wait(LPS));
   else __builtin_amdgcn_s_waitcnt(vm_wait(0));
   __builtin_amdgcn_s_barrier();
 #pragma unroll
@@ -527,14 +562,15 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
   // Step kt: matrix instructions from fa / cb; the next step's fragments into
   // fa (row block by row block, after its last use) and nb (fragment i in row
   // block i) -- on the last step a harmless read of a stale stage; with
-  // LOAD, step kt + 3's direct loads (load q in row block q) into the stage
+  // LOAD, step kt + D's direct loads (load q in row block q) into the stage
   // step kt - 1 used.  Barrier b(kt) then publishes step kt + 2 (its loads
-  // are waited for first; step kt + 3's stay in flight).  No vector register
-  // depends on a branch: the loop runs the steps that load, the last three
-  // are written out after it.
-  auto step = [&](int64_t kt, const i32x4 (&cb)[FN], i32x4 (&nb)[FN], auto load_tag)
+  // are waited for first -- WAIT of the loads issued later may stay in
+  // flight).  No vector register depends on a branch: the loop runs the
+  // steps that load, the last D are written out after it.
+  auto step = [&](int64_t kt, const i32x4 (&cb)[FN], i32x4 (&nb)[FN], auto load_tag, auto wait_tag)
       __attribute__((always_inline)) {
     constexpr bool LOAD = decltype(load_tag)::value;
+    constexpr int WAIT = decltype(wait_tag)::value;
     const int nxt = stage_of(kt + 1);
     const int lst = stage_of(kt + D);
 #pragma unroll
@@ -550,21 +586,29 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
       read_a(nxt, i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(vm_only_wait(LOAD ? LPS : 0));
+    __builtin_amdgcn_s_waitcnt(vm_only_wait(WAIT));
     __builtin_amdgcn_s_barrier();
   };
   using Load = std::integral_constant<bool, true>;
   using NoLoad = std::integral_constant<bool, false>;
-  // nsteps is even and >= 4 (the host sends other K elsewhere)
+  // in flight after a loading step's barrier: steps kt + 3 .. kt + D
+  using WaitLoad = std::integral_constant<int, (D - 2) * LPS>;
+  // nsteps is even and >= D + 1 (the host sends other K elsewhere)
   int64_t kt = 0;
-  for (; kt + 4 < nsteps; kt += 2) {
-    step(kt, fb0, fb1, Load());
-    step(kt + 1, fb1, fb0, Load());
+  for (; kt + D + 1 < nsteps; kt += 2) {
+    step(kt, fb0, fb1, Load(), WaitLoad());
+    step(kt + 1, fb1, fb0, Load(), WaitLoad());
   }
-  step(kt, fb0, fb1, Load());
-  step(kt + 1, fb1, fb0, NoLoad());
-  step(kt + 2, fb0, fb1, NoLoad());
-  step(kt + 3, fb1, fb0, NoLoad());
+  step(kt, fb0, fb1, Load(), WaitLoad());
+  // the last D steps: after step kt + 1 + r, steps up to kt + D remain
+  auto last_steps = [&](auto r_c) __attribute__((always_inline)) {
+    constexpr int r = decltype(r_c)::value;
+    using Wait = std::integral_constant<int, (D - 3 - r > 0 ? D - 3 - r : 0) * LPS>;
+    if constexpr (r % 2 == 0) step(kt + 1 + r, fb1, fb0, NoLoad(), Wait());
+    else step(kt + 1 + r, fb0, fb1, NoLoad(), Wait());
+    return true;
+  };
+  for_each_index(last_steps, std::make_integer_sequence<int, D>());
 
   // ---- epilogue (the loop's last barrier follows every LDS read of the stages)
   char *C = (char *)p.C + z * p.strideC * CE;
@@ -590,6 +634,15 @@ hipError_t launch_quad(const GemmParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN, 1 | TAIL>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, BM, BN, 0 | TAIL>), dim3((unsigned)tiles), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+// The eight-stage ring on 128x128 tiles (plain epilogue only).
+template <int AB, int CT, bool NT, int TAIL>
+hipError_t launch_quad_deep(const GemmParams &p, hipStream_t stream) {
+  const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
+  hipLaunchKernelGGL((gemm_quad_kernel<AB, CT, NT, 128, 128, TAIL | kQuadDeep>), dim3((unsigned)tiles), dim3(256),
+                     0, stream, p);
   return hipGetLastError();
 }
 

@@ -6,14 +6,15 @@
 // "GEMM to FlashAttention" page.
 //
 // HBM-bound: S*M*N*4 bytes read (the partials, each read once) and M*N
-// output elements written.  A thread takes 4 consecutive columns of a row:
-// one 16-byte load per plane when the rows are 16-byte aligned (N % 4 == 0),
-// a 4- or 8-byte store when C and its pitch allow; otherwise element by
-// element with the same order of sums.  The planes' loads are all issued
-// before the first add (S a compile-time constant up to 8, else groups of
-// 8), where a loop loading one plane and waiting before the next made each
-// thread wait S memory latencies; the whole 256 x 4096 x 4096 call with 4
-// planes went 24.55 -> 24.29 us, the pass itself taking ~6 us for its 19 MB.
+// output elements written.  A quad is 4 consecutive columns of a row: one
+// 16-byte load per plane when the rows are 16-byte aligned (N % 4 == 0), an
+// 8- or 16-byte store when C and its pitch allow; otherwise element by
+// element with the same order of sums.  For N % 4 == 0 and S <= 8 a thread
+// takes two quads and issues all 2 S loads before the first add (S a
+// compile-time constant): a loop loading one plane and waiting before the
+// next made each thread wait S memory latencies (the whole 256 x 4096 x
+// 4096 call with 4 planes: 24.55 us that way, 24.35 with one quad per
+// thread and the loads issued first, 23.9 with two).
 #include <stdint.h>
 
 #include <algorithm>
@@ -40,8 +41,69 @@ __device__ __forceinline__ void add_planes(f32x4 &a, const float *w, int64_t pla
     for (int e = 0; e < 4; ++e) a[e] = a[e] + b[u][e];
 }
 
-// SC: the number of planes when known at compile time (2 .. 8), else 0.
-template <int CT, int SC>
+template <int CT>
+__device__ __forceinline__ void store_quad_out(char *dst, const float (&v)[4], bool vec, int64_t n0, int64_t N) {
+  if (vec && n0 + 4 <= N) {
+    if constexpr (CT == kF32) {
+      *(f32x4 *)dst = f32x4{v[0], v[1], v[2], v[3]};
+    } else {
+      const uint64_t b = (uint64_t)out_bits<CT>(v[0]) | ((uint64_t)out_bits<CT>(v[1]) << 16) |
+                         ((uint64_t)out_bits<CT>(v[2]) << 32) | ((uint64_t)out_bits<CT>(v[3]) << 48);
+      *(uint64_t *)dst = b;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (n0 + e >= N) break;
+      if constexpr (CT == kF32) ((float *)dst)[e] = v[e];
+      else ((uint16_t *)dst)[e] = (uint16_t)out_bits<CT>(v[e]);
+    }
+  }
+}
+
+// Rows of 16-byte quads (N % 4 == 0) and a compile-time plane count SC: Q
+// quads per thread (a grid stride apart), all Q SC loads issued before the
+// first add.
+template <int CT, int SC, int Q>
+__global__ __launch_bounds__(256) void splitk_reduce_vec_kernel(const float *W, int64_t M, int64_t N, char *C,
+                                                                int64_t ldc, const float *bias, float scale,
+                                                                int vec_c) {
+  constexpr int CE = CT == kF32 ? 4 : 2;
+  const int64_t qpr = N >> 2;
+  const int64_t total = M * qpr;
+  const int64_t plane = M * N;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t q0 = (int64_t)blockIdx.x * 256 + threadIdx.x; q0 < total; q0 += Q * stride) {
+    f32x4 b[Q][SC];
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int64_t q = q0 + i * stride;
+      if (q < total) {
+#pragma unroll
+        for (int s = 0; s < SC; ++s) b[i][s] = __builtin_nontemporal_load((const f32x4 *)(W + s * plane + 4 * q));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int64_t q = q0 + i * stride;
+      if (q >= total) break;
+      f32x4 a = b[i][0];
+#pragma unroll
+      for (int s = 1; s < SC; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = a[e] + b[i][s][e];
+      const int64_t m = q / qpr, n0 = (q - m * qpr) * 4;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = a[e] * scale + (bias ? bias[n0 + e] : 0.f);
+      store_quad_out<CT>(C + (m * ldc + n0) * CE, v, vec_c != 0, n0, N);
+    }
+  }
+}
+
+// Any S and N: 16-byte loads where a row's quad is whole and N % 4 == 0
+// (planes in groups of 8), element by element elsewhere.
+template <int CT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *W, int64_t M, int64_t N, int S,
                                                             char *C, int64_t ldc, const float *bias,
                                                             float scale, int vec_w, int vec_c) {
@@ -56,13 +118,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *W, int6
     float v[4];
     if (vec_w && whole) {
       f32x4 a = __builtin_nontemporal_load((const f32x4 *)w);
-      if constexpr (SC > 0) {
-        add_planes<SC - 1>(a, w, plane, 1);
-      } else {
-        int s = 1;
-        for (; s + 8 <= S; s += 8) add_planes<8>(a, w, plane, s);
-        for (; s < S; ++s) add_planes<1>(a, w, plane, s);
-      }
+      int s = 1;
+      for (; s + 8 <= S; s += 8) add_planes<8>(a, w, plane, s);
+      for (; s < S; ++s) add_planes<1>(a, w, plane, s);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = a[e];
     } else {
@@ -78,23 +136,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *W, int6
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = v[e] * scale + ((bias && n0 + e < N) ? bias[n0 + e] : 0.f);
-    char *dst = C + (m * ldc + n0) * CE;
-    if (vec_c && whole) {
-      if constexpr (CT == kF32) {
-        *(f32x4 *)dst = f32x4{v[0], v[1], v[2], v[3]};
-      } else {
-        const uint64_t b = (uint64_t)out_bits<CT>(v[0]) | ((uint64_t)out_bits<CT>(v[1]) << 16) |
-                           ((uint64_t)out_bits<CT>(v[2]) << 32) | ((uint64_t)out_bits<CT>(v[3]) << 48);
-        *(uint64_t *)dst = b;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (n0 + e >= N) break;
-        if constexpr (CT == kF32) ((float *)dst)[e] = v[e];
-        else ((uint16_t *)dst)[e] = (uint16_t)out_bits<CT>(v[e]);
-      }
-    }
+    store_quad_out<CT>(C + (m * ldc + n0) * CE, v, vec_c != 0, n0, N);
   }
 }
 
@@ -107,20 +149,28 @@ hipError_t launch_typed(int64_t M, int64_t N, int S, const float *W, void *C, in
   const int64_t blocks = std::min<int64_t>((quads + 255) / 256, cap);
   const int vec_w = N % 4 == 0 ? 1 : 0;
   const int vec_c = ((uintptr_t)C % (4 * CE)) == 0 && ldc % 4 == 0 ? 1 : 0;
-#define TMM_SPLITK_LAUNCH(SC)                                                                       \
-  hipLaunchKernelGGL((splitk_reduce_kernel<CT, SC>), dim3((unsigned)blocks), dim3(256), 0, stream, W, M, N, \
-                     S, (char *)C, ldc, bias, scale, vec_w, vec_c)
-  switch (S) {
-    case 2: TMM_SPLITK_LAUNCH(2); break;
-    case 3: TMM_SPLITK_LAUNCH(3); break;
-    case 4: TMM_SPLITK_LAUNCH(4); break;
-    case 5: TMM_SPLITK_LAUNCH(5); break;
-    case 6: TMM_SPLITK_LAUNCH(6); break;
-    case 7: TMM_SPLITK_LAUNCH(7); break;
-    case 8: TMM_SPLITK_LAUNCH(8); break;
-    default: TMM_SPLITK_LAUNCH(0); break;
+  if (vec_w && S >= 2 && S <= 8) {
+    // two quads per thread (256 x 4096 x 4096 fp16, 4 slices: 24.35 -> 23.9 us
+    // per call; four quads 24.6, eight 26.7)
+    constexpr int Q = 2;
+    const int64_t nb = std::min<int64_t>((quads + 256 * Q - 1) / (256 * Q), cap);
+#define TMM_SPLITK_VEC(SC)                                                                               \
+  hipLaunchKernelGGL((splitk_reduce_vec_kernel<CT, SC, Q>), dim3((unsigned)nb), dim3(256), 0, stream, W, M, N, \
+                     (char *)C, ldc, bias, scale, vec_c)
+    switch (S) {
+      case 2: TMM_SPLITK_VEC(2); break;
+      case 3: TMM_SPLITK_VEC(3); break;
+      case 4: TMM_SPLITK_VEC(4); break;
+      case 5: TMM_SPLITK_VEC(5); break;
+      case 6: TMM_SPLITK_VEC(6); break;
+      case 7: TMM_SPLITK_VEC(7); break;
+      default: TMM_SPLITK_VEC(8); break;
+    }
+#undef TMM_SPLITK_VEC
+    return hipGetLastError();
   }
-#undef TMM_SPLITK_LAUNCH
+  hipLaunchKernelGGL((splitk_reduce_kernel<CT>), dim3((unsigned)blocks), dim3(256), 0, stream, W, M, N, S,
+                     (char *)C, ldc, bias, scale, vec_w, vec_c);
   return hipGetLastError();
 }
 

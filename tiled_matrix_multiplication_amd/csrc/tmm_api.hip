@@ -48,6 +48,10 @@ int gemv_override() {
   return (int)((ov >> 24) & 0xff) * 100 + (int)((ov >> 32) & 0xff);
 }
 int conv_override() { return (int)((override_word() >> 40) & 3); }
+int ring_override() {
+  const int r = (int)((override_word() >> 42) & 3);
+  return r == 1 ? 4 : r == 2 ? 8 : 0;
+}
 }  // namespace tmm
 
 namespace {
@@ -186,6 +190,12 @@ bool parse_override(const char *spec, uint64_t *out) {
       else if (!strcmp(val, "direct")) c = 2;
       else return false;
       v = (v & ~(3ull << 40)) | (c << 40);
+    } else if (!strcmp(key, "ring")) {
+      uint64_t c = 0;
+      if (!strcmp(val, "4")) c = 1;
+      else if (!strcmp(val, "8")) c = 2;
+      else return false;
+      v = (v & ~(3ull << 42)) | (c << 42);
     } else {
       return false;
     }

@@ -17,6 +17,10 @@ int gemv_override();
 // four-wave kernel, 2 the register-direct one.
 int conv_override();
 
+// Ring depth of the four-wave kernel on 128x128 tiles pinned by the
+// override: 0 none, else 4 or 8 stages.
+int ring_override();
+
 // Element formats, same numbering as tmm_dtype in include/tmm.h.
 enum Fmt : int { kF32 = 0, kBF16 = 1, kF16 = 2, kF8 = 3 };
 
