@@ -109,3 +109,28 @@ def test_ragged_shape_takes_the_tail_form(tmm, force):
     force("128x128q", ring=8)
     dC2, _, _ = gemm_case(tmm, M, N, K, "bf16", "bf16", False, "normal", False, seed=7500)
     assert torch.equal(dC.view(torch.int16), dC2.view(torch.int16))
+
+
+def _draw(i):
+    g = np.random.default_rng([20261203, i])
+    fmt = ["bf16", "f16"][g.integers(0, 2)]
+    out = [fmt, "f32"][g.integers(0, 2)]
+    tb = bool(g.integers(0, 2))
+    M, N, K = int(g.integers(1, 600)), int(g.integers(8, 600)), int(g.integers(129, 1400))
+    pad = int(g.choice([0, 0, 1, 3, 8]))
+    dist = ["normal", "int"][g.integers(0, 2)]
+    bias = bool(g.integers(0, 2))
+    tile, ring = TILES[g.integers(0, len(TILES))]
+    return M, N, K, fmt, out, tb, dist, bias, pad, tile, ring
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_random_shapes_on_the_four_wave_forms(tmm, force, i):
+    """Seeded random shapes (any K from 129, rows at any alignment, ragged M
+    and N) on the four- and eight-stage 128x128 tiles, the 256x128 tiles and
+    the automatic choice."""
+    M, N, K, fmt, out, tb, dist, bias, pad, tile, ring = _draw(i)
+    force(tile, ring=ring)
+    dC, o, T = gemm_case(tmm, M, N, K, fmt, out, tb, dist, bias, seed=90000 + 10 * i, pad=pad)
+    check(dC, o, T, K, exact=(dist == "int"),
+          what=f"{M}x{N}x{K} {fmt}->{out} {'NT' if tb else 'NN'} pad {pad} {dist} tile {tile} ring {ring}")
