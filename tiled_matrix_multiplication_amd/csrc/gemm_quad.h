@@ -3,7 +3,7 @@
 // waves): the kernel for 16-bit inputs, rows at any element alignment, whose
 // K is a multiple of 64, at least 128 -- or, in its K-tail form (kQuadTail),
 // any K with at least 128 below its last 64-element boundary, the last
-// elements of K read by words before the main loop.
+// elements of K loaded and multiplied before the main loop.
 //
 //   C[z] = act(scale * A[z] . op(B[z]) (+ bias) (+ beta * old C[z])),
 //   row-major, z < batch, act = identity or ReLU
@@ -463,18 +463,17 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmParams p) {
     // holding a valid element (load8_u16_tail: a chunk that K or N cuts is
     // loaded from where its last valid element ends it and shifted into
     // place, so no read leaves the operands: K - KT >= 128, and a cut NN row
-    // holds N >= 8 elements; five word loads per chunk instead cost 3.4 of
-    // the 22.6 us of 4097 x 511 x 1023 NN bf16); then the ring's first D
-    // steps go out as in the plain form, and the
-    // tail passes one step at a time through the last stage (which the
-    // ring's first step reloads), in the ring's layout, each published by a
-    // barrier, multiplied, and released by a second one.  Its loads' latency
-    // runs under the ring's.  The ring's loads stay below k-row K - KT:
-    // whole chunks inside every row of A (and of a K-contiguous B), and for
-    // an NN B the chunk a row's end cuts through reads at most 7 elements
-    // into the next k-row (which exists, and holds N >= 8 elements, checked
-    // by the host); those columns past N feed only outputs that are never
-    // stored.
+    // holds N >= 8 elements).  Then the ring's first D steps go out as in
+    // the plain form, and the tail passes one step at a time through the
+    // last stage (which the ring's first step reloads), in the ring's
+    // layout: a barrier publishes it, the waves multiply it, a second
+    // barrier releases the stage.  The ring's loads stay below k-row
+    // K - KT: whole chunks inside every row of A (and of a K-contiguous B),
+    // and for an NN B the chunk a row's end cuts through reads at most 7
+    // elements into the next k-row (which exists, and holds N >= 8
+    // elements, checked by the host); those columns past N feed only
+    // outputs that are never stored.  The tail's loads cost ~3.5 of the
+    // 22 us of 4097 x 511 x 1023 NN bf16 (timing copies without them).
     const int64_t k0 = K - KT;
     constexpr int TQA = BM * 8 / 256;                      // tail chunks per thread (A)
     constexpr int TQB = NT ? BN * 8 / 256 : 64 * CPR / 256;  // (B)
