@@ -27,6 +27,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -609,13 +610,23 @@ def kernel_family(name):
     return "gemm"
 
 
+def code_without_comments(text):
+    """C++ source with // and /* */ comments and blank runs removed (string
+    literals in these sources hold no comment markers), so that an edit to a
+    comment does not count as a change of the kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(name):
-    """Hash of the sources of the workload's kernel: counter-derived traffic
-    is only reported for the kernel code it was measured on."""
+    """Hash of the code (comments aside) of the workload's kernel sources:
+    counter-derived traffic is only reported for the kernel code it was
+    measured on."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel_family(name)]:
         h.update(f.encode())
-        h.update(open(os.path.join(CSRC, f), "rb").read())
+        h.update(code_without_comments(open(os.path.join(CSRC, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

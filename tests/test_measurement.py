@@ -77,3 +77,15 @@ def test_headline_work_and_bytes():
 def test_gpus_above_one_are_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_traffic_hash_ignores_comments_only():
+    """A committed traffic figure stays valid across comment edits of its
+    kernel's sources and is dropped when the code itself changes."""
+    src = "int a = 1; // one\n/* block\n comment */ int b = 2;\n\n  // only a comment\nint c;\n"
+    same = "int a = 1;   // another remark\n/* other */ int b = 2;\nint c;\n"
+    changed = "int a = 2;\nint b = 2;\nint c;\n"
+    strip = bench.code_without_comments
+    assert strip(src) == strip(same.replace("   ", " "))
+    assert strip(src) != strip(changed)
+    assert "//" not in strip(src) and "/*" not in strip(src)
