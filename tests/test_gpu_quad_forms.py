@@ -1,10 +1,11 @@
 """GPU parity of the four-wave kernel's K-tail form (gemm_quad.h, kQuadTail)
 and of its eight-stage ring on 128x128 tiles (kQuadDeep) against the
 oracle.  K-tail form: K not a multiple of 64, its last K mod 64 elements
-(one or two 32-element steps) read by words before the main loop, and NN B
-rows that end inside a 16-byte chunk (the last 64 k-rows read that way when
-64 divides K).  Each case runs on the 128x128 tiles with four and with eight
-ring stages, on the 256x128 tiles and through the automatic choice; rows at
+(one or two 32-element steps) loaded and multiplied before the main loop,
+and NN B rows that end inside a 16-byte chunk (the last 64 k-rows taken that
+way when 64 divides K).  Each case runs on the 128x128 tiles with four and
+with eight ring stages, on the 256x128 and 256x256 tiles and through the
+automatic choice; rows at
 2-byte alignment (odd K or N, odd padding), ragged M and N, every output
 type, bias, the plain, ReLU and beta forms, batches, and small integers held
 bit for bit.  Shapes just outside a form (K - (K mod 64) < 128, fewer than 8
@@ -23,7 +24,7 @@ from test_gpu_gemm_ex import run_case
 pytestmark = pytest.mark.gpu
 
 # (tile, ring stages): None = the automatic choice
-TILES = [("128x128q", 4), ("128x128q", 8), ("256x128q", None), (None, None)]
+TILES = [("128x128q", 4), ("128x128q", 8), ("256x128q", None), ("256x256q", None), (None, None)]
 
 # (M, N, K, in, out, trans_b, dist, bias, pad)
 CASES = [

@@ -894,12 +894,18 @@ hipError_t launch_tile(Tile tile, bool vec, const GemmParams &p, hipStream_t str
       case kTile256x256:
       case kTile256x256q:
         // Four-wave kernel (gemm_quad.h): 16-bit inputs, an even number (at
-        // least 4) of 32-element K-steps, the plain or full form.  Chosen for every
-        // such 256x256 tile: it measured faster than the ring and two-stage
-        // kernels at every shape timed (4096^3 NN fp32 out 118.1 -> 102.3 us;
-        // 8192x12288x4096 NT 661.6 -> 621.5 us; 8192^3 NN 880 -> 765 us).
+        // least 4) of 32-element K-steps or the K-tail form, the plain or
+        // full form.  Chosen for every such 256x256 tile: it measured faster
+        // than the ring and two-stage kernels at every shape timed (4096^3
+        // NN fp32 out 118.1 -> 102.3 us; 8192x12288x4096 NT 661.6 -> 621.5
+        // us; 8192^3 NN 880 -> 765 us).
         if constexpr (AB == kBF16 || AB == kF16) {
-          if (quad_form<NT>(p, 2) == 0) return launch_quad<AB, CT, NT, 256, 256, 0>(p, stream);
+          const int form = quad_form<NT>(p, 2);
+          if (form == 0) return launch_quad<AB, CT, NT, 256, 256, 0>(p, stream);
+          if (form > 0) return launch_quad<AB, CT, NT, 256, 256, 4>(p, stream);
+          // an NN B cut inside a chunk that the K-tail form does not take:
+          // the two-stage kernel (the ring below loads whole chunks)
+          if (!NT && (p.N * 2) % 16 != 0) return launch_one<AB, CT, NT, 256, 256, 8, true>(p, stream);
         }
         // fp8: the four-wave kernel of gemm_quad8.h (an even number, at least
         // 4, of 64-element K-steps; the plain form): 8192^3 NN bf16 out

@@ -417,10 +417,11 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
     // words, see load_words.h).  So 16-bit and fp32 operands need no more
     // than their element alignment for the tiled kernels (rows of
     // 1000 x 3000 x 777 or 4097 x 511 x 1023 bf16).  An NN B whose rows end
-    // inside a 16-byte chunk (N * e % 16 != 0) stays off the ring and the
-    // 256 x 256 four-wave kernel, whose direct loads move whole chunks up to
-    // the last k-row; the narrower four-wave tiles take it in their K-tail
-    // form (launch_tile), which reads the last k-rows by words.
+    // inside a 16-byte chunk (N * e % 16 != 0) stays off the ring kernel,
+    // whose direct loads move whole chunks up to the last k-row; the
+    // four-wave kernel takes it in its K-tail form (launch_tile), which
+    // loads the last 64 k-rows itself, and the two-stage kernel where that
+    // form does not apply.
     const bool elem16 = ab == TMM_BF16 || ab == TMM_F16 || ab == TMM_F32;
     const bool loads16 = vec || elem16;
     const bool nn_cut = !trans_b && (N * e) % 16 != 0;
@@ -452,10 +453,7 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
       err = tmm::launch_gemm_skinny((Fmt)ab, (Fmt)c, bm, bn, vec_c, p, stream);
     } else {
       tmm::Tile tile = loads16 ? pick_tile(M, N, batch, ab) : tmm::kTile128x128;
-      if (nn_cut) {  // the 256 x 256 direct-load kernels need whole NN B chunks
-        if (tile == tmm::kTile256x256 || tile == tmm::kTile256x256r || tile == tmm::kTile256x256q)
-          tile = tmm::kTile256x256s2;
-      }
+      if (nn_cut && tile == tmm::kTile256x256r) tile = tmm::kTile256x256s2;  // the ring needs whole NN B chunks
       err = dispatch_gemm(ab, c, trans_b != 0, tile, loads16, p, stream);
     }
   }
