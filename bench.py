@@ -588,6 +588,7 @@ KERNEL_SOURCES = {
     "splitk": ["gemm_mfma.h", "gemm_ring.h", "gemm_quad.h", "gemm_quad8.h", "load_words.h", "gemm_f32.hip",
                "gemm_bf16.hip", "gemm_f16.hip", "gemm_f8.hip", "gemm_ring_ta.hip", "gemm_short_k.hip",
                "splitk.hip"],
+    "f32small": ["gemm_f32_small.hip"],
 }
 
 
@@ -607,6 +608,8 @@ def kernel_family(name):
         return "gemv" if WORKLOADS[name][0] <= GEMV_MULTI_MAX_M else "skinny"
     if name in CONV:
         return "conv"
+    if name == "f32_256":
+        return "f32small"   # fp32 256^3: the small-product kernel (gemm_f32_small.hip)
     return "gemm"
 
 

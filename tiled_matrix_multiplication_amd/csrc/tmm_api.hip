@@ -451,6 +451,12 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
       const int ce = elem_bytes(c);
       const bool vec_c = aligned(C, 4 * ce) && ldc % 4 == 0 && (batch == 1 || sC % 4 == 0);
       err = tmm::launch_gemm_skinny((Fmt)ab, (Fmt)c, bm, bn, vec_c, p, stream);
+    } else if (ab == TMM_F32 && f < 0 && !generic_forced &&
+               ((M + 127) / 128) * ((N + 127) / 128) * batch * 2 <= cu_count()) {
+      // fp32 with at most one 128x128 tile per two CUs: 32x32 tiles with K
+      // split over a workgroup's waves (fp32 256^3: 21.2 us on four 128x128
+      // tiles)
+      err = tmm::launch_gemm_f32_small(trans_b != 0, p, stream);
     } else {
       tmm::Tile tile = loads16 ? pick_tile(M, N, batch, ab) : tmm::kTile128x128;
       if (nn_cut && tile == tmm::kTile256x256r) tile = tmm::kTile256x256s2;  // the ring needs whole NN B chunks

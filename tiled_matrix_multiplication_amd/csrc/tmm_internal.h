@@ -69,6 +69,10 @@ inline int tile_bn(Tile t) {
 // `vec` selects the 16-byte-load path (every operand row 16-byte aligned);
 // otherwise element loads are used (128x128 tiles).  Returns hipSuccess or
 // the launch error.
+// fp32 products of few 128x128 tiles: 32x32 tiles, K split over the four
+// waves of a workgroup (gemm_f32_small.hip); plain or full form.
+hipError_t launch_gemm_f32_small(bool trans_b, const GemmParams &p, hipStream_t stream);
+
 hipError_t launch_gemm_f32(Fmt c, bool trans_b, Tile tile, bool vec, const GemmParams &p,
                            hipStream_t stream);
 hipError_t launch_gemm_bf16(Fmt c, bool trans_b, Tile tile, bool vec, const GemmParams &p,
