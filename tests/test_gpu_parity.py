@@ -163,6 +163,24 @@ def test_short_k_kernel(tmm, force, Z, M, N, K, fmt):
     assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), "short-K and two-stage kernels differ"
 
 
+def test_short_k_pitched_output(tmm, force):
+    """The short-K kernel writing into a view of a wider and taller buffer
+    (row pitch N + 64, batch stride past the view's rows): bit for bit the
+    two-stage kernel's result, and nothing outside the view is written."""
+    Z, M, N, K = 3, 512, 512, 128
+    A, B = _batched_nt(Z, M, N, K, "f16", 91)
+    force("shortk")
+    big = torch.full((Z, M + 16, N + 64), float("nan"), dtype=torch.float16, device=DEV)
+    view = big[:, 8:8 + M, 32:32 + N]
+    tmm.tmm_gemm_strided_batched(on_gpu(A, "f16"), on_gpu(B, "f16"), view, trans_b=True)
+    torch.cuda.synchronize()
+    ref = _run_batched_nt(tmm, A, B, "f16", "256x256s2", force)
+    assert torch.equal(view.contiguous().view(torch.int16), ref.view(torch.int16)), "pitched short-K output differs"
+    outside = torch.ones(big.shape, dtype=torch.bool, device=DEV)
+    outside[:, 8:8 + M, 32:32 + N] = False
+    assert bool(torch.isnan(big[outside]).all()), "short-K kernel wrote outside its output view"
+
+
 def test_attention_scores_shape_takes_short_k(tmm, force):
     """Short K over many whole tiles (64 problems x 16 tiles, K = 128) is what
     the dispatch sends to the short-K kernel without forcing: the result
