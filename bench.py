@@ -580,14 +580,14 @@ CSRC = os.path.join(ROOT, "tiled_matrix_multiplication_amd", "csrc")
 # the shared parameter header are not part of it).
 KERNEL_SOURCES = {
     "gemm": ["gemm_mfma.h", "gemm_ring.h", "gemm_quad.h", "gemm_quad8.h", "load_words.h", "gemm_f32.hip",
-             "gemm_bf16.hip", "gemm_f16.hip", "gemm_f8.hip", "gemm_ring_ta.hip", "gemm_short_k.hip"],
+             "gemm_bf16.hip", "gemm_f16.hip", "gemm_f8.hip", "gemm_ring_ta.hip"],
+    "shortk": ["gemm_mfma.h", "gemm_ring.h", "gemm_short_k.hip"],
     "gemv": ["gemv.hip"],
     "skinny": ["gemm_skinny.hip"],
     "attention": ["attention.hip"],
     "conv": ["conv_implicit.hip", "conv_quad.h", "gemm_quad.h", "gemm_ring.h", "gemm_mfma.h"],
     "splitk": ["gemm_mfma.h", "gemm_ring.h", "gemm_quad.h", "gemm_quad8.h", "load_words.h", "gemm_f32.hip",
-               "gemm_bf16.hip", "gemm_f16.hip", "gemm_f8.hip", "gemm_ring_ta.hip", "gemm_short_k.hip",
-               "splitk.hip"],
+               "gemm_bf16.hip", "gemm_f16.hip", "gemm_f8.hip", "gemm_ring_ta.hip", "splitk.hip"],
     "f32small": ["gemm_f32_small.hip"],
 }
 
@@ -610,6 +610,8 @@ def kernel_family(name):
         return "conv"
     if name == "f32_256":
         return "f32small"   # fp32 256^3: the small-product kernel (gemm_f32_small.hip)
+    if name == "attn_scores":
+        return "shortk"     # Q.K^T over whole 256x256 tiles: the persistent short-K kernel
     return "gemm"
 
 
