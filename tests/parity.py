@@ -27,7 +27,7 @@ Tolerances (the pages give none; these follow from the arithmetic):
         s_a s_b ( |sum_k sign(p_k) d_k| / 2 + LAMBDA_F8 sqrt(sum_k d_k^2 / 12) ),
     (f_k taken as uniform on [0, d_k)), added to the fp32 allowance above,
     and never more than the worst case s_a s_b sum_k d_k.  Beyond the
-    elementwise rule, the benchmark spec's fp8 figure 1e-3 is held as a relative
+    elementwise rule, the fp8 target's 1e-3 is held as a relative
     Frobenius error on every 32x32 block (an accumulator tile), so an error
     confined to one block cannot hide in the whole matrix's norm.
   * the elements accepted only by an allowance beyond 1 ulp are counted;
