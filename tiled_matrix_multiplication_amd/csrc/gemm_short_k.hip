@@ -18,16 +18,21 @@
 //   * eight waves own 128x64 blocks of the tile as 4x2 32x32 accumulators
 //     (v_mfma_f32_32x32x16 over K/16 slices), as in the two-stage kernel;
 //   * after the last matrix instruction and a barrier, the waves issue the
-//     next tile's direct loads into the operand area and only then stage
-//     and store this tile (store_tile_tr below, through each wave's own
-//     4 KiB past the operands: 160 KiB in all at K = 128), so the loads are
-//     ahead of the stores in the memory pipeline;
-//   * a wave then waits with vmcnt(number of its stores): the loads, issued
-//     first, are complete while the stores may still be draining, and the
-//     next tile's matrix work overlaps them.  This is why the loads are
-//     written as assembly (untracked by the compiler, which would otherwise
-//     wait for everything) and why the host sends only whole tiles here:
-//     every wave issues exactly FM * 4 stores per tile.
+//     next tile's direct loads into the operand area, then stage and store
+//     the first 32-row band of their block (band_out below, through each
+//     wave's own 4 KiB past the operands: 160 KiB in all at K = 128) and
+//     keep the other three bands as packed 16-bit values (48 registers);
+//     those go out during the next tile's matrix work, one band after each
+//     quarter of its K slices, so that their staging runs while the matrix
+//     pipe is busy instead of after it;
+//   * a wave then waits with vmcnt(4), its first band's stores: the loads,
+//     issued before them, are complete (and so are the previous tile's
+//     bands, issued before the loads), while these stores may still be
+//     draining.  This is why the loads are written as assembly (untracked
+//     by the compiler, which would otherwise wait for everything) and why
+//     the host sends only whole tiles here: every wave issues exactly 4
+//     stores per band.  The loads take 32-bit offsets from a wave-uniform
+//     base (the host keeps lda and ldb below 2^22).
 // No bias, no scale (the plain 16-bit form); anything else takes the
 // general kernels.
 #include "gemm_ring.h"
@@ -35,6 +40,12 @@
 namespace tmm {
 namespace gemm_detail {
 namespace {
+
+// 16-byte direct global->LDS load of base + off (base wave-uniform, off this
+// lane's 32-bit byte offset); lane L's 16 bytes land at LDS byte m0 + 16 L.
+__device__ __forceinline__ void dma16_off(const char *base, uint32_t off, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
 
 template <int RB>
 __device__ __forceinline__ int sk_swz(int row) {
@@ -68,52 +79,57 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 __device__ __forceinline__ int tr_swz(int m) { return ((m & 3) << 1) ^ (3 * ((m >> 2) & 1)); }
 __device__ __forceinline__ int tr_pos(int n, int u) { return n * 64 + ((u ^ tr_swz((n >> 2) & 7)) << 3); }
 
-// Stores a wave's FM x 2 accumulator blocks (rows row0 + 32 i + ..., columns
-// col0 .. col0 + 63) as 16-bit values, one 32x64 band at a time through the
-// wave's own 4 KiB of LDS at st.  Lane (l32, g) writes, for each 4-row group
-// of its column, the four values as one 8-byte unit (4 writes per block
-// instead of 16 two-byte writes).  The transposing read ds_read_b64_tr_b16
-// gives lane j of a 16-lane group element j % 4 of the units addressed by
-// lanes j / 4, 4 + j / 4, 8 + j / 4 and 12 + j / 4; with lane 4 k + a
-// addressing column c0 + 8 a + 4 t + k at the unit of rows R0 .. R0 + 3,
-// lane 4 a + b receives row R0 + b, columns c0 + 8 a + 4 t .. + 3, and two
-// reads (t = 0, 1) make its 16-byte row piece.  One store instruction then
-// writes 8 whole 128-byte rows (two groups per 4 rows, 32 columns each), as
-// a row-major staging would, FM * 4 stores per wave.  Whole tiles only, C
-// and its pitch 16-byte aligned (the host's conditions for this kernel).
-template <int CT, int FM>
-__device__ __forceinline__ void store_tile_tr(const f32x16 (&acc)[FM][2], char *st, char *C, int64_t ldc,
-                                              int64_t row0, int64_t col0, int lane) {
+// Stores one 32x64 band (rows row0 .., columns col0 .. col0 + 63) of 16-bit
+// values from its packed form w[j][q]: lane (l32, g) holds, for column
+// 32 j + l32 and row group q, rows 8 q + 4 g .. + 3 as one 8-byte unit (two
+// words), written to the wave's 4 KiB staging area st in one instruction
+// per unit (4 per 32x32 block instead of 16 two-byte writes).  The
+// transposing read ds_read_b64_tr_b16 gives lane j of a 16-lane group
+// element j % 4 of the units addressed by lanes j / 4, 4 + j / 4, 8 + j / 4
+// and 12 + j / 4; with lane 4 k + a addressing column c0 + 8 a + 4 t + k at
+// the unit of rows R0 .. R0 + 3, lane 4 a + b receives row R0 + b, columns
+// c0 + 8 a + 4 t .. + 3, and two reads (t = 0, 1) make its 16-byte row
+// piece.  One store instruction then writes 8 whole 128-byte rows (two
+// groups per 4 rows, 32 columns each).  Whole tiles only, C and its pitch
+// 16-byte aligned (the host's conditions for this kernel).
+__device__ __forceinline__ void band_out(const uint32_t (&w)[2][4][2], char *st, char *C, int64_t ldc,
+                                         int64_t row0, int64_t col0, int lane) {
   const int l32 = lane & 31, g = lane >> 5;
   const int G = lane >> 4, i16 = lane & 15;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int q = 0; q < 4; ++q)
+      *(i32x2 *)(st + tr_pos(32 * j + l32, 2 * q + g)) = i32x2{(int)w[j][q][0], (int)w[j][q][1]};
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // accumulator r = 4 q + e: row 8 q + 4 g + e of the band, column 32 j + l32
-        const f32x16 &a = acc[i][j];
-        const uint32_t w0 = pack2<CT>(a[4 * q], a[4 * q + 1]);
-        const uint32_t w1 = pack2<CT>(a[4 * q + 2], a[4 * q + 3]);
-        *(i32x2 *)(st + tr_pos(32 * j + l32, 2 * q + g)) = i32x2{(int)w0, (int)w1};
-      }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-    __builtin_amdgcn_wave_barrier();
+  for (int s = 0; s < 4; ++s) {
+    const int r0 = 8 * s + 4 * ((G & 1) ^ (G >> 1)), c0 = 32 * (G >> 1);
+    i32x2 h[2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      // groups 0 and 3 take rows R0 = 8 s .. + 3, groups 1 and 2 the next four
-      const int r0 = 8 * s + 4 * ((G & 1) ^ (G >> 1)), c0 = 32 * (G >> 1);
-      i32x2 h[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        h[t] = __builtin_bit_cast(
-            i32x2, lds_read_tr16(st + tr_pos(c0 + 8 * (i16 & 3) + 4 * t + (i16 >> 2), r0 >> 2)));
-      const i32x4 v = {h[0][0], h[0][1], h[1][0], h[1][1]};
-      char *dst = C + ((row0 + i * 32 + r0 + (i16 & 3)) * ldc + col0 + c0 + 8 * (i16 >> 2)) * 2;
-      __builtin_nontemporal_store(v, (i32x4 *)dst);   // written once, not read back here
-    }
+    for (int t = 0; t < 2; ++t)
+      h[t] = __builtin_bit_cast(
+          i32x2, lds_read_tr16(st + tr_pos(c0 + 8 * (i16 & 3) + 4 * t + (i16 >> 2), r0 >> 2)));
+    const i32x4 v = {h[0][0], h[0][1], h[1][0], h[1][1]};
+    char *dst = C + ((row0 + r0 + (i16 & 3)) * ldc + col0 + c0 + 8 * (i16 >> 2)) * 2;
+    __builtin_nontemporal_store(v, (i32x4 *)dst);
   }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the staging area is written again
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The packed form of a band held in accumulators a[0..1] (accumulator
+// r = 4 q + e of lane (l32, g): row 8 q + 4 g + e, column 32 j + l32).
+template <int CT>
+__device__ __forceinline__ void pack_band(const f32x16 (&a)[2], uint32_t (&w)[2][4][2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[j][q][0] = pack2<CT>(a[j][4 * q], a[j][4 * q + 1]);
+      w[j][q][1] = pack2<CT>(a[j][4 * q + 2], a[j][4 * q + 3]);
+    }
 }
 
 template <int AB, int KE>
@@ -130,10 +146,8 @@ __global__ __launch_bounds__(512, 1) void gemm_short_k_kernel(GemmParams p) {
   constexpr int RPL = 1024 / RB;                  // rows per direct-load instruction
   constexpr int LOADS = OPS / 1024 / NW;          // direct loads per wave per tile
   constexpr int SLICES = KE / 16;
-  constexpr int NSTORE = FM * (32 * (WTN * 2 / 16) / 64);  // store instructions per wave per tile
   static_assert(KE == 64 || KE == 128, "short-K kernel: K = 64 or 128");
   static_assert(LOADS * RPL * NW == BM + BN, "direct-load geometry");
-  static_assert(NSTORE <= 63, "vmcnt range");
   static_assert(FN == 2 && WTN == 64 && CT != kF32, "epilogue geometry: 32x64 bands of 16-bit values");
   static_assert(OPS + NW * STG <= 160 * 1024, "LDS");
 
@@ -151,10 +165,6 @@ __global__ __launch_bounds__(512, 1) void gemm_short_k_kernel(GemmParams p) {
   const int64_t total = per * p.batch;
 
   const uint32_t lds0 = lds_addr(lds);
-  // This lane's part of each direct load: operand row (of the 512 A then B
-  // rows) wave * LOADS * RPL + i * RPL + lane / CPR, LDS position lane % CPR,
-  // which holds logical chunk (lane % CPR) ^ f(row).
-  const int pos = lane % CPR;
 
   auto tile_of = [&](int64_t t, int64_t &z, int64_t &m0, int64_t &n0) __attribute__((always_inline)) {
     int64_t pid = remap_xcd(t, total);
@@ -171,19 +181,36 @@ __global__ __launch_bounds__(512, 1) void gemm_short_k_kernel(GemmParams p) {
     tile_of(t, z, m0, n0);
     const char *A = (const char *)p.A + (z * p.strideA + m0 * p.lda) * E;
     const char *B = (const char *)p.B + (z * p.strideB + n0 * p.ldb) * E;
+    // This lane's part of load i: operand row (of the 512 A then B rows)
+    // wave * LOADS * RPL + i * RPL + lane / CPR, LDS position lane % CPR,
+    // which holds logical chunk (lane % CPR) ^ f(row).  The offsets are
+    // recomputed for every tile (cheap) rather than kept in 16 registers
+    // across the loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lpos = ln % CPR;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int first = (wave * LOADS + i) * RPL;   // wave-uniform
-      const int row = first + lane / CPR;
-      const int chunk = pos ^ sk_swz<RB>(row);
-      const char *src = row < BM ? A + ((int64_t)row * p.lda * E + chunk * 16)
-                                 : B + ((int64_t)(row - BM) * p.ldb * E + chunk * 16);
-      dma16(src, lds0 + first * RB);
+      const int row = first + ln / CPR;
+      const int chunk = lpos ^ sk_swz<RB>(row);
+      if (first < BM)
+        dma16_off(A, (uint32_t)(row * (uint32_t)(p.lda * E)) + chunk * 16, lds0 + first * RB);
+      else
+        dma16_off(B, (uint32_t)((row - BM) * (uint32_t)(p.ldb * E)) + chunk * 16, lds0 + first * RB);
     }
   };
 
   int64_t t = blockIdx.x;
   if (t >= total) return;
+  // bands FM - HOLD .. FM - 1 of the previous tile, packed, stored during this tile's slices
+  constexpr int HOLD = 3;
+  static_assert(HOLD < FM && SLICES % (HOLD + 1) == 0, "held bands");
+  uint32_t pk[HOLD][2][4][2];
+  char *pC = nullptr;
+  int64_t prow0 = 0, pcol0 = 0;
+  bool have_prev = false;
+  char *const st = lds + OPS + wave * STG;
   issue(t);
   __builtin_amdgcn_s_waitcnt(vm_wait(0));
   __syncthreads();
@@ -225,6 +252,12 @@ __global__ __launch_bounds__(512, 1) void gemm_short_k_kernel(GemmParams p) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                 __builtin_bit_cast(f16x8, fa[i]), __builtin_bit_cast(f16x8, fb[j]), acc[i][j], 0, 0, 0);
         }
+      constexpr int SPB = SLICES / (HOLD + 1);   // slices per held band
+      if ((s + 1) % SPB == 0 && (s + 1) / SPB <= HOLD) {
+        const int h = (s + 1) / SPB - 1;         // held band h: band FM - HOLD + h of the previous tile
+        if (have_prev) band_out(pk[h], st, pC, p.ldc, prow0 + 32 * (FM - HOLD + h), pcol0, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // Every wave's operand reads are done: the area takes the next tile.
@@ -234,11 +267,26 @@ __global__ __launch_bounds__(512, 1) void gemm_short_k_kernel(GemmParams p) {
     if (more) issue(next);
 
     char *C = (char *)p.C + z * p.strideC * E;
-    store_tile_tr<CT, FM>(acc, lds + OPS + wave * STG, C, p.ldc, m0 + wm * WTM, n0 + wn * WTN, lane);
-    if (!more) break;
-    // The loads were issued before this wave's NSTORE stores: with at most
-    // NSTORE operations outstanding they are complete.
-    __builtin_amdgcn_s_waitcnt(vm_wait(NSTORE));
+#pragma unroll
+    for (int b = 0; b < FM - HOLD; ++b) {
+      uint32_t w0[2][4][2];
+      pack_band<CT>(acc[b], w0);
+      band_out(w0, st, C, p.ldc, m0 + wm * WTM + 32 * b, n0 + wn * WTN, lane);
+    }
+#pragma unroll
+    for (int h = 0; h < HOLD; ++h) pack_band<CT>(acc[FM - HOLD + h], pk[h]);
+    pC = C;
+    prow0 = m0 + wm * WTM;
+    pcol0 = n0 + wn * WTN;
+    have_prev = true;
+    if (!more) {
+#pragma unroll
+      for (int h = 0; h < HOLD; ++h) band_out(pk[h], st, pC, p.ldc, prow0 + 32 * (FM - HOLD + h), pcol0, lane);
+      break;
+    }
+    // In issue order: the previous tile's held bands, this tile's loads,
+    // this tile's first bands: with their stores outstanding the loads are in.
+    __builtin_amdgcn_s_waitcnt(vm_wait(4 * (FM - HOLD)));
     __syncthreads();
     t = next;
   }

@@ -333,13 +333,16 @@ bool use_ring_ta(int64_t M, int64_t N, int64_t batch) {
 // form, aligned rows and C.  Chosen automatically with at least four tiles
 // per CU (a write-bound product: batched 2048 x 2048 x 128 fp16, the
 // attention scores, 272 us on the two-stage kernel); "shortk" forces it.
-bool short_k_ok(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const void *C,
-                int64_t ldc, int64_t sC, int64_t batch, const float *bias, bool plain, bool vec) {
+bool short_k_ok(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, int64_t lda, int64_t ldb,
+                const void *C, int64_t ldc, int64_t sC, int64_t batch, const float *bias, bool plain,
+                bool vec) {
   const int f = forced_tile();
   if (f >= 0 && !forced_short_k()) return false;
   if (!vec || !trans_b || !plain || bias || c != ab || (ab != TMM_BF16 && ab != TMM_F16)) return false;
   if ((K != 64 && K != 128) || M % 256 != 0 || N % 256 != 0) return false;
   if (!aligned(C, 16) || (ldc * 2) % 16 != 0 || (batch > 1 && (sC * 2) % 16 != 0)) return false;
+  // the kernel's load offsets within a tile's 256 rows are 32-bit
+  if (lda >= ((int64_t)1 << 22) || ldb >= ((int64_t)1 << 22)) return false;
   if (forced_short_k()) return true;
   return (M / 256) * (N / 256) * batch >= 4 * (int64_t)cu_count();
 }
@@ -440,7 +443,7 @@ int run_gemm(int64_t M, int64_t N, int64_t K, int ab, int c, int trans_b, const 
       g.N = N; g.K = K; g.W = B; g.ldw = ldb; g.x = A; g.ldx = lda; g.M = M;
       g.y = C; g.ldy = ldc; g.bias = bias;
       err = tmm::launch_gemv_multi((Fmt)ab, (Fmt)c, g, stream);
-    } else if (short_k_ok(M, N, K, ab, c, trans_b, C, ldc, sC, batch, bias, plain, vec)) {
+    } else if (short_k_ok(M, N, K, ab, c, trans_b, lda, ldb, C, ldc, sC, batch, bias, plain, vec)) {
       const int64_t total = (M / 256) * (N / 256) * batch;
       const int64_t cus = cu_count();
       const unsigned grid = (unsigned)std::max<int64_t>(8, std::min<int64_t>(total, cus) / 8 * 8);
